@@ -1,0 +1,241 @@
+"""Benchmark of the MoE layer forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral_t512]
+
+A step is one whole layer (routing, count/scan, permutation, fused gate+up
+SwiGLU grouped GEMM, down grouped GEMM, combine) over one batch of seeded
+synthetic input, replayed from a hipGraph with every input already resident
+in HBM.  Prints one JSON line with tokens/s, the grouped-GEMM MFMA and HBM
+fractions, the roofline of the dominant kernel (the fused gate+up GEMM, timed
+with HIP events on the stream it runs on) and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s @Mixtral shape T=512; grouped-GEMM % MFMA / % HBM peak"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_F32_TFLOPS = 157.3      # MI355X fp32 vector/matrix, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_t512")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    ap.add_argument("--kernel-iters", type=int, default=20)
+    return ap.parse_args()
+
+
+def gemm_work(wl, counts, dt_bytes):
+    """Algorithmic FLOPs and HBM bytes of the two grouped GEMMs (per launch)."""
+    Tk = wl.T * wl.k
+    active = int((counts > 0).sum())
+    gu_flops = 4.0 * Tk * wl.d * wl.F
+    dn_flops = 2.0 * Tk * wl.d * wl.F
+    gu_bytes = (active * 2.0 * wl.F * wl.d + Tk * wl.d + Tk * wl.F) * dt_bytes
+    dn_bytes = (active * 1.0 * wl.F * wl.d + Tk * wl.F + Tk * wl.d) * dt_bytes
+    return gu_flops, gu_bytes, dn_flops, dn_bytes, active
+
+
+def cpu_baseline(wl, inp, sample_tokens):
+    """The oracle as it stands, on the first `sample_tokens` tokens."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe_oracle as O
+    n = min(wl.T, sample_tokens)
+    cores = min(16, os.cpu_count() or 1)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        if inp.topk_ids is None:
+            O.forward(inp.x[:n], inp.wr, inp.wg, inp.wu, inp.wd, wl.k, wl.dtype, bias=inp.bias,
+                      capacity=wl.capacity)
+        else:
+            O.forward(inp.x[:n], inp.wr, inp.wg, inp.wu, inp.wd, wl.k, wl.dtype,
+                      topk_ids=inp.topk_ids[:n], topk_w=inp.topk_w[:n], capacity=wl.capacity)
+        dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {wl.T} tokens of {wl.name} (seed 0), whole layer in float64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); "
+              "the layer is not sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import grouped_gemm_gemv_amd as M
+    from workloads import get_workload, make_inputs
+
+    wl = get_workload(args.workload)
+    log(f"workload {wl.name}: generating inputs (seed {args.seed})")
+    t0 = time.time()
+    inp = make_inputs(wl, args.seed)
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+    torch.cuda.set_device(0)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dt_bytes = 2 if wl.dtype == "bf16" else 4
+
+    def dev(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    x, wr, bias = dev(inp.x), dev(inp.wr), dev(inp.bias)
+    wg, wu, wd = dev(inp.wg), dev(inp.wu), dev(inp.wd)
+    ids_in, w_in = dev(inp.topk_ids), dev(inp.topk_w)
+    shape = M.Shape(wl.T, wl.d, wl.E, wl.k, wl.F, wl.capacity, dt)
+    q = M.query(shape)
+    ws = M.workspace(q.forward_ws_bytes)
+    out = torch.empty((wl.T, wl.d), dtype=dt, device="cuda")
+
+    def step():
+        return M.moe_forward(shape, x, wr, bias, ids_in, w_in, wg, wu, wd, out, ws)
+
+    views = step()
+    torch.cuda.synchronize()
+    counts = views.disp.arrays()["counts"].cpu().numpy()
+    log(f"eager forward ok; tile rows {q.tile_rows}, counts {counts.tolist()[:16]}")
+
+    # graph capture of the whole layer (no host sync, no allocation inside)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"{args.steps} graph replays: {ms * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step)")
+
+    # per-call times (HIP events on the stream the kernels run on)
+    cur = torch.cuda.current_stream()
+    disp = views.disp
+    h, y, xp = views.h, views.y_perm, views.x_perm
+    pws = M.workspace(q.permute_ws_bytes)
+    ids = views.topk_ids
+    wts = views.topk_w
+
+    def timed(fn, iters):
+        for _ in range(3):
+            fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        cur.synchronize()
+        a.record(cur)
+        for _ in range(iters):
+            fn()
+        b.record(cur)
+        b.synchronize()
+        return a.elapsed_time(b) / iters * 1e3  # us
+
+    it = args.kernel_iters
+    passes = q.n_passes
+    t_gu = sum(timed(lambda p=p: M.moe_ffn_gate_up(shape, xp, wg, wu, disp, p, h), it) for p in range(passes))
+    t_dn = sum(timed(lambda p=p: M.moe_ffn_down(shape, h, wd, disp, p, y), it) for p in range(passes))
+    t_perm = timed(lambda: M.moe_permute(shape, x, ids, disp, xp, pws), it)
+    t_comb = timed(lambda: M.moe_combine(shape, y, wts, disp, out), it)
+    t_route = 0.0
+    if ids_in is None:
+        rid = torch.empty_like(ids)
+        rw = torch.empty_like(wts)
+        t_route = timed(lambda: M.moe_route(shape, x, wr, bias, rid, rw), it)
+    log(f"per call (us): route {t_route:.1f} permute {t_perm:.1f} gate_up {t_gu:.1f} down {t_dn:.1f} "
+        f"combine {t_comb:.1f}")
+
+    gu_flops, gu_bytes, dn_flops, dn_bytes, active = gemm_work(wl, counts, dt_bytes)
+    peak_f = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if gu_flops / gu_bytes < ridge:
+        ach = gu_bytes / (t_gu * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        ach = gu_flops / (t_gu * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_f, "unit": "TFLOP/s",
+                "frac": round(ach / peak_f, 4), "traffic": None}
+    roof["kernel"] = "grouped_gemm_kernel (fused gate+up SwiGLU)"
+    roof["us_per_launch"] = round(t_gu / passes, 2)
+    roof["algorithmic_bytes"] = gu_bytes
+    roof["algorithmic_flops"] = gu_flops
+    t_gemm = (t_gu + t_dn) * 1e-6
+    gemm_flops = gu_flops + dn_flops
+    gemm_bytes = gu_bytes + dn_bytes
+    gg = {
+        "us": round(t_gu + t_dn, 1),
+        "tflops": round(gemm_flops / t_gemm / 1e12, 1),
+        "mfma_frac": round(gemm_flops / t_gemm / 1e12 / peak_f, 4),
+        "gbps": round(gemm_bytes / t_gemm / 1e9, 1),
+        "hbm_frac": round(gemm_bytes / t_gemm / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline_frac": round(max(gemm_flops / (peak_f * 1e12), gemm_bytes / (PEAK_HBM_GBS * 1e9)) / t_gemm, 4),
+        "active_experts": active,
+    }
+    tokens_per_s = wl.T / (ms * 1e-3)
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded normal draws, random-init weights)",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "F": wl.F,
+                   "capacity": wl.capacity, "seed": args.seed, "graph": True},
+        "grouped_gemm": gg,
+        "per_call_us": {"route": round(t_route, 1), "permute": round(t_perm, 1), "gate_up": round(t_gu, 1),
+                        "down": round(t_dn, 1), "combine": round(t_comb, 1)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,24 @@
+"""MI355X-native single-GPU MoE layer forward pass (libmoe + thin binding).
+
+The HIP library is loaded on first use; importing the package does not touch
+the GPU.
+"""
+from .api import (
+    Dispatch,
+    ForwardViews,
+    Shape,
+    moe_combine,
+    moe_ffn_down,
+    moe_ffn_gate_up,
+    moe_forward,
+    moe_grouped_ffn,
+    moe_permute,
+    moe_route,
+    query,
+    workspace,
+)
+
+__all__ = [
+    "Dispatch", "ForwardViews", "Shape", "moe_combine", "moe_ffn_down", "moe_ffn_gate_up", "moe_forward",
+    "moe_grouped_ffn", "moe_permute", "moe_route", "query", "workspace",
+]

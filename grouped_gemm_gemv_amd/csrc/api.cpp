@@ -1,0 +1,378 @@
+// C ABI of libmoe: host-side validation, sizing, workspace layout and kernel
+// enqueue.  Nothing here allocates, frees or synchronises; every validation
+// error is returned before the first HIP call.
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "launch.hpp"
+#include "moe.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Rows per tile of the grouped GEMMs: the smallest supported height that
+// covers the expected rows of an active expert (T*k spread over
+// min(E, T*k) experts, at most C in the capacity pass), so that the common
+// expert needs one row tile and its weights stream from HBM once.
+int choose_tile_rows(const moe_shape_t& s) {
+  const int64_t Tk = (int64_t)s.T * s.k;
+  int64_t mean = ceil_div(Tk, std::min<int64_t>(s.E, Tk));
+  if (s.capacity > 0) mean = std::min<int64_t>(mean, s.capacity);
+  if (mean <= 16) return 16;
+  if (mean <= 32) return 32;
+  if (mean <= 64) return 64;
+  return 128;
+}
+
+int64_t spill_bound(const moe_shape_t& s) { return std::max<int64_t>(0, (int64_t)s.T * s.k - s.capacity); }
+
+// Upper bound on the tiles of one pass: a pass of R_p rows over at most E_p
+// non-empty experts has sum ceil(r_e / BM) <= (R_p + E_p (BM - 1)) / BM.
+int64_t pass_max_tiles(const moe_shape_t& s, int BM, int pass) {
+  const int64_t Tk = (int64_t)s.T * s.k;
+  if (s.capacity <= 0) {
+    if (pass == 1) return 0;
+    return (Tk + std::min<int64_t>(s.E, Tk) * (BM - 1)) / BM;
+  }
+  const int64_t C = s.capacity;
+  if (pass == 0) {
+    const int64_t Rp = std::min<int64_t>(Tk, (int64_t)s.E * C);
+    return std::min<int64_t>((Rp + std::min<int64_t>(s.E, Tk) * (BM - 1)) / BM, (int64_t)s.E * ceil_div(C, BM));
+  }
+  const int64_t Ep = std::min<int64_t>(s.E, Tk / (C + 1));  // overflowing experts hold >= C+1 entries
+  return (spill_bound(s) + Ep * (BM - 1)) / BM;
+}
+
+int64_t row_space(const moe_shape_t& s) {
+  if (s.capacity <= 0) return (int64_t)s.T * s.k;
+  return (int64_t)s.E * s.capacity + spill_bound(s);
+}
+
+size_t elt_bytes(const moe_shape_t& s) { return s.dtype == MOE_BF16 ? 2 : 4; }
+
+moe_status_t validate(const moe_shape_t* s) {
+  if (s == nullptr) return MOE_ERR_NULL_PTR;
+  if (s->T < 1 || s->E < 1 || s->E > 256 || s->k < 1 || s->k > s->E || s->k > 64 || s->capacity < 0 ||
+      s->d < 64 || s->F < 64)
+    return MOE_ERR_INVALID_ARG;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->d % 64 != 0 || s->F % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t Tk = (int64_t)s->T * s->k;
+  if (Tk >= INT32_MAX) return MOE_ERR_INVALID_ARG;
+  const int64_t R = row_space(*s);
+  if (R >= INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)s->E * s->capacity >= INT32_MAX) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// Layout of the dispatch buffer (byte offsets from its base).
+struct DispatchLayout {
+  size_t counts, offsets, spill_counts, spill_offsets, row_of, token_of, tile_off, tile_map, n_tiles, err_flags;
+  size_t bytes;
+};
+
+struct Plan {
+  int64_t Tk, R;
+  int BM;
+  int64_t max_tiles;      // stride of each pass in tile_map
+  int64_t pass_tiles[2];  // grid bound of each pass
+  int nblk;
+  DispatchLayout dl;
+  size_t permute_ws;      // block counts + block error flags
+  size_t ws_ids, ws_w, ws_disp, ws_perm, ws_xperm, ws_h, ws_y, forward_ws;
+};
+
+Plan make_plan(const moe_shape_t& s) {
+  Plan p{};
+  p.Tk = (int64_t)s.T * s.k;
+  p.R = row_space(s);
+  p.BM = choose_tile_rows(s);
+  p.pass_tiles[0] = pass_max_tiles(s, p.BM, 0);
+  p.pass_tiles[1] = pass_max_tiles(s, p.BM, 1);
+  p.max_tiles = std::max<int64_t>(1, std::max(p.pass_tiles[0], p.pass_tiles[1]));
+  p.nblk = (int)ceil_div(p.Tk, moe::kCountChunk);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t E = (size_t)s.E;
+  p.dl.counts = take(4 * E);
+  p.dl.offsets = take(4 * (E + 1));
+  p.dl.spill_counts = take(4 * E);
+  p.dl.spill_offsets = take(4 * (E + 1));
+  p.dl.row_of = take(4 * (size_t)p.Tk);
+  p.dl.token_of = take(4 * (size_t)p.R);
+  p.dl.tile_off = take(4 * 2 * (E + 1));
+  p.dl.tile_map = take(4 * 4 * 2 * (size_t)p.max_tiles);
+  p.dl.n_tiles = take(4 * 2);
+  p.dl.err_flags = take(4);
+  p.dl.bytes = o;
+  p.permute_ws = align_up(4 * (size_t)p.nblk * E) + align_up(4 * (size_t)p.nblk);
+  const size_t eb = elt_bytes(s);
+  o = 0;
+  p.ws_ids = take(4 * (size_t)p.Tk);
+  p.ws_w = take(4 * (size_t)p.Tk);
+  p.ws_disp = take(p.dl.bytes);
+  p.ws_perm = take(p.permute_ws);
+  p.ws_xperm = take((size_t)p.R * s.d * eb);
+  p.ws_h = take((size_t)p.R * s.F * eb);
+  p.ws_y = take((size_t)p.R * s.d * eb);
+  p.forward_ws = o;
+  return p;
+}
+
+void carve(const moe_shape_t& s, const Plan& p, char* base, moe_dispatch_t* d) {
+  d->counts = reinterpret_cast<int32_t*>(base + p.dl.counts);
+  d->offsets = reinterpret_cast<int32_t*>(base + p.dl.offsets);
+  d->spill_counts = reinterpret_cast<int32_t*>(base + p.dl.spill_counts);
+  d->spill_offsets = reinterpret_cast<int32_t*>(base + p.dl.spill_offsets);
+  d->row_of = reinterpret_cast<int32_t*>(base + p.dl.row_of);
+  d->token_of = reinterpret_cast<int32_t*>(base + p.dl.token_of);
+  d->tile_off = reinterpret_cast<int32_t*>(base + p.dl.tile_off);
+  d->tile_map = reinterpret_cast<int32_t*>(base + p.dl.tile_map);
+  d->n_tiles = reinterpret_cast<int32_t*>(base + p.dl.n_tiles);
+  d->err_flags = reinterpret_cast<uint32_t*>(base + p.dl.err_flags);
+  d->tile_rows = p.BM;
+  d->max_tiles = (int32_t)p.max_tiles;
+  (void)s;
+}
+
+moe_status_t check_dispatch(const moe_shape_t& s, const Plan& p, const moe_dispatch_t* d) {
+  if (d == nullptr) return MOE_ERR_NULL_PTR;
+  if (!d->counts || !d->offsets || !d->spill_counts || !d->spill_offsets || !d->row_of || !d->token_of ||
+      !d->tile_off || !d->tile_map || !d->n_tiles || !d->err_flags)
+    return MOE_ERR_NULL_PTR;
+  if (d->tile_rows != 16 && d->tile_rows != 32 && d->tile_rows != 64 && d->tile_rows != 128)
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t need = std::max(pass_max_tiles(s, d->tile_rows, 0), pass_max_tiles(s, d->tile_rows, 1));
+  if (d->max_tiles < need || d->max_tiles < 1) return MOE_ERR_INVALID_ARG;
+  (void)p;
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status_t enqueue_permute(const moe_shape_t& s, const Plan& p, const void* x, const int32_t* ids,
+                             const moe_dispatch_t& d, void* x_perm, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  int32_t* block_counts = reinterpret_cast<int32_t*>(w);
+  uint32_t* block_err = reinterpret_cast<uint32_t*>(w + align_up(4 * (size_t)p.nblk * s.E));
+  const int Tk = (int)p.Tk;
+  hipError_t e = moe::launch_count(ids, Tk, s.E, p.nblk, block_counts, block_err, d.token_of, p.R, st);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  moe::ScanArgs a;
+  a.block_counts = block_counts;
+  a.block_err = block_err;
+  a.nblk = p.nblk;
+  a.E = s.E;
+  a.C = s.capacity;
+  a.BM = d.tile_rows;
+  a.max_tiles = d.max_tiles;
+  a.counts = d.counts;
+  a.offsets = d.offsets;
+  a.spill_counts = d.spill_counts;
+  a.spill_offsets = d.spill_offsets;
+  a.tile_off = d.tile_off;
+  a.tile_map = d.tile_map;
+  a.n_tiles = d.n_tiles;
+  a.err_flags = d.err_flags;
+  if ((e = moe::launch_scan(a, st)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = moe::launch_scatter(ids, Tk, s.k, s.E, s.capacity, p.nblk, block_counts, d.offsets, d.spill_offsets,
+                               d.row_of, d.token_of, st)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return hip_status(moe::launch_gather(x, d.row_of, Tk, s.k, (int64_t)s.d * elt_bytes(s), x_perm, st));
+}
+
+moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass, bool gated) {
+  moe::GemmArgs a{};
+  a.tile_off = d.tile_off + pass * (s.E + 1);
+  a.tile_map = d.tile_map + (size_t)pass * d.max_tiles * 4;
+  a.n_tiles = d.n_tiles + pass;
+  a.E = s.E;
+  a.K = gated ? s.d : s.F;
+  a.N = gated ? s.F : s.d;
+  a.max_tiles = (int)pass_max_tiles(s, d.tile_rows, pass);
+  return a;
+}
+
+moe_status_t enqueue_gate_up(const moe_shape_t& s, const void* x_perm, const void* wg, const void* wu,
+                             const moe_dispatch_t& d, int pass, void* h, hipStream_t st) {
+  moe::GemmArgs a = gemm_args(s, d, pass, true);
+  a.act = x_perm;
+  a.w0 = wg;
+  a.w1 = wu;
+  a.out = h;
+  return hip_status(moe::launch_grouped_gemm(s.dtype, true, d.tile_rows, a, st));
+}
+
+moe_status_t enqueue_down(const moe_shape_t& s, const void* h, const void* wd, const moe_dispatch_t& d, int pass,
+                          void* y, hipStream_t st) {
+  moe::GemmArgs a = gemm_args(s, d, pass, false);
+  a.act = h;
+  a.w0 = wd;
+  a.w1 = nullptr;
+  a.out = y;
+  return hip_status(moe::launch_grouped_gemm(s.dtype, false, d.tile_rows, a, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: a shape field or size is out of range";
+    case MOE_ERR_NULL_PTR: return "MOE_ERR_NULL_PTR: a required pointer is NULL";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace below the queried size";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid arguments this build does not implement";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+    default: return "unknown moe_status_t";
+  }
+}
+
+moe_status_t moe_query(const moe_shape_t* s, moe_sizes_t* out) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (out == nullptr) return MOE_ERR_NULL_PTR;
+  const Plan p = make_plan(*s);
+  out->rows = p.R;
+  out->tile_rows = p.BM;
+  out->max_tiles = (int32_t)p.max_tiles;
+  out->n_passes = s->capacity > 0 ? 2 : 1;
+  out->count_blocks = p.nblk;
+  out->dispatch_bytes = p.dl.bytes;
+  out->permute_ws_bytes = p.permute_ws;
+  out->forward_ws_bytes = p.forward_ws;
+  return MOE_OK;
+}
+
+moe_status_t moe_dispatch_carve(const moe_shape_t* s, void* base, size_t bytes, moe_dispatch_t* disp) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (base == nullptr || disp == nullptr) return MOE_ERR_NULL_PTR;
+  const Plan p = make_plan(*s);
+  if (bytes < p.dl.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (reinterpret_cast<uintptr_t>(base) % kAlign != 0) return MOE_ERR_INVALID_ARG;
+  carve(*s, p, static_cast<char*>(base), disp);
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
+                       int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_NULL_PTR;
+  return hip_status(moe::launch_route(s->dtype, x, w_router, bias, s->T, s->d, s->E, s->k, topk_ids, topk_w, stream));
+}
+
+moe_status_t moe_permute(const moe_shape_t* s, const void* x, const int32_t* topk_ids, const moe_dispatch_t* disp,
+                         void* x_perm, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (!x || !topk_ids || !x_perm || !workspace) return MOE_ERR_NULL_PTR;
+  const Plan p = make_plan(*s);
+  if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
+  if (ws_bytes < p.permute_ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return enqueue_permute(*s, p, x, topk_ids, *disp, x_perm, workspace, stream);
+}
+
+moe_status_t moe_ffn_gate_up(const moe_shape_t* s, const void* x_perm, const void* w_gate, const void* w_up,
+                             const moe_dispatch_t* disp, int pass, void* h, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !w_gate || !w_up || !h) return MOE_ERR_NULL_PTR;
+  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(*s);
+  if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
+  return enqueue_gate_up(*s, x_perm, w_gate, w_up, *disp, pass, h, stream);
+}
+
+moe_status_t moe_ffn_down(const moe_shape_t* s, const void* h, const void* w_down, const moe_dispatch_t* disp,
+                          int pass, void* y_perm, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (!h || !w_down || !y_perm) return MOE_ERR_NULL_PTR;
+  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(*s);
+  if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
+  return enqueue_down(*s, h, w_down, *disp, pass, y_perm, stream);
+}
+
+moe_status_t moe_grouped_ffn(const moe_shape_t* s, const void* x_perm, const void* w_gate, const void* w_up,
+                             const void* w_down, const moe_dispatch_t* disp, void* h, void* y_perm,
+                             hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !w_gate || !w_up || !w_down || !h || !y_perm) return MOE_ERR_NULL_PTR;
+  const Plan p = make_plan(*s);
+  if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
+  const int passes = s->capacity > 0 ? 2 : 1;
+  for (int ps = 0; ps < passes; ++ps) {
+    if ((st = enqueue_gate_up(*s, x_perm, w_gate, w_up, *disp, ps, h, stream)) != MOE_OK) return st;
+    if ((st = enqueue_down(*s, h, w_down, *disp, ps, y_perm, stream)) != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm, const float* topk_w, const moe_dispatch_t* disp,
+                         void* out, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !topk_w || !out) return MOE_ERR_NULL_PTR;
+  if (disp == nullptr) return MOE_ERR_NULL_PTR;
+  if (!disp->row_of) return MOE_ERR_NULL_PTR;
+  return hip_status(moe::launch_combine(s->dtype, y_perm, topk_w, disp->row_of, s->T, s->k, s->d, out, stream));
+}
+
+moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
+                         const int32_t* topk_ids_in, const float* topk_w_in, const void* w_gate, const void* w_up,
+                         const void* w_down, void* out, void* workspace, size_t ws_bytes,
+                         moe_forward_views_t* views_out, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (!x || !w_gate || !w_up || !w_down || !out || !workspace) return MOE_ERR_NULL_PTR;
+  if ((topk_ids_in == nullptr) != (topk_w_in == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (topk_ids_in == nullptr && w_router == nullptr) return MOE_ERR_NULL_PTR;
+  const Plan p = make_plan(*s);
+  if (ws_bytes < p.forward_ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return MOE_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  moe_forward_views_t v{};
+  carve(*s, p, ws + p.ws_disp, &v.disp);
+  v.x_perm = ws + p.ws_xperm;
+  v.h = ws + p.ws_h;
+  v.y_perm = ws + p.ws_y;
+  if (topk_ids_in != nullptr) {
+    v.topk_ids = const_cast<int32_t*>(topk_ids_in);
+    v.topk_w = const_cast<float*>(topk_w_in);
+  } else {
+    v.topk_ids = reinterpret_cast<int32_t*>(ws + p.ws_ids);
+    v.topk_w = reinterpret_cast<float*>(ws + p.ws_w);
+  }
+  if (views_out != nullptr) *views_out = v;
+  if (topk_ids_in == nullptr) {
+    if (moe::launch_route(s->dtype, x, w_router, bias, s->T, s->d, s->E, s->k, v.topk_ids, v.topk_w, stream) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if ((st = enqueue_permute(*s, p, x, v.topk_ids, v.disp, v.x_perm, ws + p.ws_perm, stream)) != MOE_OK) return st;
+  const int passes = s->capacity > 0 ? 2 : 1;
+  for (int ps = 0; ps < passes; ++ps) {
+    if ((st = enqueue_gate_up(*s, v.x_perm, w_gate, w_up, v.disp, ps, v.h, stream)) != MOE_OK) return st;
+    if ((st = enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream)) != MOE_OK) return st;
+  }
+  return hip_status(
+      moe::launch_combine(s->dtype, v.y_perm, v.topk_w, v.disp.row_of, s->T, s->k, s->d, out, stream));
+}
+
+}  // extern "C"

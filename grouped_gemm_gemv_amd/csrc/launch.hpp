@@ -1,0 +1,67 @@
+// Kernel launchers of libmoe (internal; called by api.cpp after validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Entries handled by one block of the counting and scatter kernels.
+constexpr int kCountChunk = 2048;
+// Tokens per block of the router kernel.
+constexpr int kRouteTokens = 16;
+
+hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* bias, int T, int d,
+                        int E, int k, int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+hipError_t launch_count(const int32_t* ids, int Tk, int E, int nblk, int32_t* block_counts,
+                        uint32_t* block_err, int32_t* token_of, int64_t fill_rows, hipStream_t stream);
+
+struct ScanArgs {
+  int32_t* block_counts;  // [nblk][E] in: per-block counts; out: per-block base ranks
+  const uint32_t* block_err;
+  int nblk, E, C, BM, max_tiles;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* spill_counts;
+  int32_t* spill_offsets;
+  int32_t* tile_off;  // [2][E+1]
+  int32_t* tile_map;  // [2][max_tiles][4]
+  int32_t* n_tiles;   // [2]
+  uint32_t* err_flags;
+};
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+
+hipError_t launch_scatter(const int32_t* ids, int Tk, int k, int E, int C, int nblk,
+                          const int32_t* block_base, const int32_t* offsets, const int32_t* spill_offsets,
+                          int32_t* row_of, int32_t* token_of, hipStream_t stream);
+
+hipError_t launch_gather(const void* x, const int32_t* row_of, int Tk, int k, int64_t row_bytes,
+                         void* x_perm, hipStream_t stream);
+
+hipError_t launch_combine(int dtype, const void* y, const float* topk_w, const int32_t* row_of, int T,
+                          int k, int d, void* out, hipStream_t stream);
+
+struct GemmArgs {
+  const void* act;           // [R][K] activation rows
+  const void* w0;            // [E][N][K]
+  const void* w1;            // [E][N][K] (gate+up: the up projection), else null
+  void* out;                 // [R][N]
+  const int32_t* tile_off;   // [E+1] of this pass
+  const int32_t* tile_map;   // [max_tiles][4] of this pass
+  const int32_t* n_tiles;    // [1] of this pass
+  int E, K, N;
+  int max_tiles;
+};
+
+// Tile shape of the grouped GEMMs for a tile height and problem.
+struct GemmTiling {
+  int BM;       // rows per tile
+  int cols;     // output columns per workgroup
+  int threads;  // workgroup size
+};
+GemmTiling gemm_tiling(int BM, bool gated, int N);
+
+hipError_t launch_grouped_gemm(int dtype, bool gated, int BM, const GemmArgs& a, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,205 @@
+/*
+ * moe.h -- C ABI of libmoe, a single-GPU Mixture-of-Experts layer forward
+ * pass for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the five-stage pipeline named in the TritonMoE review
+ * (pith.science verdict for arXiv 2605.23911, referee summary): router
+ * scoring, token permutation, expert GEMMs (a fused gate+up SwiGLU GEMM, then
+ * the down projection) and weighted unpermutation.  The expert GEMMs are a
+ * block-scheduled grouped GEMM: fixed-size row tiles mapped to (expert, row
+ * offset) pairs (that review's Algorithm 1, section 3.2), with the map built
+ * on the device.  An optional capacity-bounded dispatch follows the
+ * Cap-and-Spill critique (juhe.plus, section "Cap-and-Spill"): a first pass
+ * of at most C rows per expert and a second pass over the overflow,
+ * compacted into one buffer whose size is fixed in advance; no token is
+ * dropped and nothing is read back to the host.
+ *
+ * Conventions (every entry point):
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns and
+ *    allocates every buffer, including workspaces; the library never
+ *    allocates, frees or synchronises, and keeps no mutable global state.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting.  Every call can be captured into a
+ *    hipGraph: grids depend only on the shape, never on device data.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    validation error nothing is enqueued and no HIP call is made.  After
+ *    enqueueing, a launch failure reported by hipGetLastError is returned as
+ *    MOE_ERR_HIP.
+ *  - Matrices are row-major.  x, the router and expert weights, the permuted
+ *    activations, the SwiGLU intermediate, the expert outputs and the layer
+ *    output all have the element type `dtype` (fp32 or bf16); routing weights
+ *    are always fp32 and indices int32.  Accumulation is fp32.
+ *  - Results are bitwise reproducible run to run on one device: no floating
+ *    point atomics; every reduction has a fixed order.
+ *
+ * Shape limits: T >= 1; 1 <= k <= E <= 256; k <= 64; d and F multiples of
+ * 64; T*k and every row-space index below 2^31.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,        /* a shape field or size is out of range      */
+  MOE_ERR_NULL_PTR = 2,           /* a required pointer is NULL                 */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes below what moe_query reports      */
+  MOE_ERR_UNSUPPORTED = 4,        /* valid but not implemented (dtype, tile)    */
+  MOE_ERR_HIP = 5                 /* a kernel launch failed                     */
+} moe_status_t;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Problem shape.  capacity = 0: uncapped dispatch; capacity = C >= 1:
+ * capacity-bounded dispatch with an overflow pass. */
+typedef struct moe_shape {
+  int32_t T;        /* tokens                                  */
+  int32_t d;        /* model width                             */
+  int32_t E;        /* experts                                 */
+  int32_t k;        /* experts per token                       */
+  int32_t F;        /* expert FFN width                        */
+  int32_t capacity; /* C, or 0                                 */
+  int32_t dtype;    /* moe_dtype_t                             */
+} moe_shape_t;
+
+/* Sizes derived from a shape (all host values). */
+typedef struct moe_sizes {
+  int64_t rows;             /* R: rows of x_perm / h / y_perm.  T*k uncapped;
+                               E*C + max(0, T*k - C) with capacity C (fixed
+                               region of C rows per expert, then the overflow
+                               region; the overflow never exceeds T*k - C)   */
+  int32_t tile_rows;        /* BM: rows per tile of the grouped GEMMs        */
+  int32_t max_tiles;        /* tile_map entries reserved per pass            */
+  int32_t n_passes;         /* 1 uncapped, 2 with capacity                   */
+  int32_t count_blocks;     /* work blocks of the counting step              */
+  size_t dispatch_bytes;    /* bytes for moe_dispatch_carve                  */
+  size_t permute_ws_bytes;  /* workspace of moe_permute                      */
+  size_t forward_ws_bytes;  /* workspace of moe_forward (includes all of the
+                               above plus x_perm, h, y_perm, ids, weights)   */
+} moe_sizes_t;
+
+/* Dispatch metadata (device arrays), produced by moe_permute and read by the
+ * grouped FFN and the combine.  Entry f = t*k + j names slot j of token t.
+ * Pass 0 is the uncapped row space or the fixed region; pass 1 the overflow
+ * region (empty when uncapped). */
+typedef struct moe_dispatch {
+  int32_t* counts;         /* [E]      n_e: entries routed to expert e           */
+  int32_t* offsets;        /* [E+1]    exclusive scan of counts                  */
+  int32_t* spill_counts;   /* [E]      o_e = max(0, n_e - C); zero when uncapped */
+  int32_t* spill_offsets;  /* [E+1]    exclusive scan of spill_counts            */
+  int32_t* row_of;         /* [T*k]    row of entry f; -1 if its id was invalid  */
+  int32_t* token_of;       /* [R]      token of each row; -1 for unused rows     */
+  int32_t* tile_off;       /* [2][E+1] per pass: exclusive scan of tiles/expert  */
+  int32_t* tile_map;       /* [2][max_tiles][4] per pass: {expert, first row,
+                              rows in tile (1..BM), tile index within expert}  */
+  int32_t* n_tiles;        /* [2]      tiles in pass 0 and pass 1                */
+  uint32_t* err_flags;     /* [1]      bit 0: an id outside [0, E) was skipped   */
+  int32_t tile_rows;       /* BM the tile map was built for                      */
+  int32_t max_tiles;       /* entries reserved per pass in tile_map              */
+} moe_dispatch_t;
+
+/* Human-readable name of a status code (host; static storage). */
+const char* moe_status_string(int status);
+
+/* Fill `out` (host) with the sizes for shape `s` (host).  Host arithmetic
+ * only.  Errors: MOE_ERR_NULL_PTR, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED. */
+moe_status_t moe_query(const moe_shape_t* s, moe_sizes_t* out);
+
+/* Point the arrays of `disp` (host struct) into the device buffer `base` of
+ * `bytes` bytes (>= moe_sizes_t.dispatch_bytes; 256-byte aligned).  Host
+ * only; nothing is written to the device. */
+moe_status_t moe_dispatch_carve(const moe_shape_t* s, void* base, size_t bytes, moe_dispatch_t* disp);
+
+/* Router scoring and top-k softmax routing (TritonMoE review, referee
+ * summary: "router scoring" ahead of permutation).
+ *   logits[t,e] = sum_i x[t,i] * w_router[e,i] + (bias ? bias[e] : 0)   (fp32)
+ *   topk_ids[t, 0..k-1] = the k largest logits, largest first; equal logits
+ *                         ordered by the lower expert index
+ *   topk_w[t, j] = softmax over all E, taken at topk_ids[t,j] and
+ *                  renormalised over the k chosen (sums to 1)
+ * x [T,d], w_router [E,d] (dtype); bias [E] fp32 or NULL; topk_ids [T,k]
+ * int32; topk_w [T,k] fp32. */
+moe_status_t moe_route(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
+                       int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* Count, exclusive scan, stable permutation, capacity split, tile map and
+ * the gather of token rows into expert-contiguous order (TritonMoE review,
+ * referee summary: token permutation; Algorithm 1 block schedule;
+ * Cap-and-Spill critique, section "Cap-and-Spill").
+ *   counts/offsets: histogram and exclusive scan of topk_ids.
+ *   Stable order: inside an expert, entries keep ascending f (ascending token).
+ *   Uncapped: row_of[f] = offsets[e] + rank(f).
+ *   Capacity C: rank < C -> row e*C + rank (fixed region);
+ *               rank >= C -> row E*C + spill_offsets[e] + rank - C.
+ *   x_perm[row_of[f]] = x[f / k] (bit copy); unused rows are not written.
+ * topk_ids [T,k]; x [T,d]; disp from moe_dispatch_carve; x_perm [R,d];
+ * workspace of >= permute_ws_bytes (contents need no initialisation). */
+moe_status_t moe_permute(const moe_shape_t* s, const void* x, const int32_t* topk_ids,
+                         const moe_dispatch_t* disp, void* x_perm, void* workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Fused gate+up SwiGLU grouped GEMM over one pass's tile map (TritonMoE
+ * review, key machinery: both projections from one load of each input tile,
+ * SiLU in registers, no gate/up intermediates in memory):
+ *   h[r, n] = silu(g) * u,  g = sum_i x_perm[r,i] * w_gate[e,n,i],
+ *             u = sum_i x_perm[r,i] * w_up[e,n,i],  silu(z) = z / (1 + exp(-z))
+ * for every row r of every tile (e, ...) of pass `pass` (0 or 1).
+ * x_perm [R,d]; w_gate, w_up [E,F,d]; h [R,F]; h is rounded to dtype. */
+moe_status_t moe_ffn_gate_up(const moe_shape_t* s, const void* x_perm, const void* w_gate,
+                             const void* w_up, const moe_dispatch_t* disp, int pass, void* h,
+                             hipStream_t stream);
+
+/* Down-projection grouped GEMM over one pass's tile map (TritonMoE review,
+ * desk-editor letter: the down projection is a separate kernel):
+ *   y_perm[r, o] = sum_n h[r,n] * w_down[e,o,n]
+ * h [R,F]; w_down [E,d,F]; y_perm [R,d] (rounded to dtype). */
+moe_status_t moe_ffn_down(const moe_shape_t* s, const void* h, const void* w_down,
+                          const moe_dispatch_t* disp, int pass, void* y_perm, hipStream_t stream);
+
+/* Both expert GEMMs over every pass: gate+up then down for pass 0, then (with
+ * capacity) for pass 1. */
+moe_status_t moe_grouped_ffn(const moe_shape_t* s, const void* x_perm, const void* w_gate,
+                             const void* w_up, const void* w_down, const moe_dispatch_t* disp,
+                             void* h, void* y_perm, hipStream_t stream);
+
+/* Weighted unpermutation (TritonMoE review, referee summary):
+ *   out[t] = sum_{j=0..k-1} topk_w[t,j] * y_perm[row_of[t*k+j]]
+ * accumulated in fp32 in ascending j and rounded once to dtype; entries
+ * with row_of = -1 contribute nothing.  y_perm [R,d]; topk_w [T,k];
+ * out [T,d]. */
+moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm, const float* topk_w,
+                         const moe_dispatch_t* disp, void* out, hipStream_t stream);
+
+/* Where moe_forward keeps its intermediates inside the workspace (device
+ * pointers; valid until the workspace is reused). */
+typedef struct moe_forward_views {
+  moe_dispatch_t disp;  /* dispatch arrays                                     */
+  int32_t* topk_ids;    /* [T,k] routing used (computed, or a copy of the input) */
+  float* topk_w;        /* [T,k]                                               */
+  void* x_perm;         /* [R,d]                                               */
+  void* h;              /* [R,F]                                               */
+  void* y_perm;         /* [R,d]                                               */
+} moe_forward_views_t;
+
+/* The whole layer on one stream: route (unless topk_ids_in and topk_w_in are
+ * given; both or neither), permute, grouped FFN (both passes with capacity),
+ * combine.  No host synchronisation and no allocation: every intermediate
+ * lives in `workspace` (>= forward_ws_bytes).  If views_out (host) is not
+ * NULL it receives where the intermediates live inside the workspace. */
+moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
+                         const int32_t* topk_ids_in, const float* topk_w_in, const void* w_gate,
+                         const void* w_up, const void* w_down, void* out, void* workspace,
+                         size_t ws_bytes, moe_forward_views_t* views_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -325,7 +325,7 @@ def forward(x, wr, wg, wu, wd, k: int, dtype: str, bias=None, topk_ids=None, top
         res["logits"] = lg
     else:
         ids = np.asarray(topk_ids, dtype=np.int32)
-        w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+        w = np.asarray(topk_w, dtype=np.float64)  # fp32 inputs widen exactly
     E = np.asarray(wr).shape[0]
     disp = dispatch(ids, E, capacity, tile_rows)
     y = expert_outputs(x, wg, wu, wd, dtype, disp, ids)

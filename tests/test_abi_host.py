@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI (no GPU): exports, sizing and validation.
+
+Every call here either is host arithmetic (moe_query, moe_dispatch_carve,
+moe_status_string) or fails validation, which returns before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from grouped_gemm_gemv_amd import _lib
+from grouped_gemm_gemv_amd._lib import MoeDispatch, MoeForwardViews, MoeShape, MoeSizes
+from oracle import moe_oracle as O
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmoe.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status_t|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_lib.EXPORTED) == names
+
+
+def test_status_strings():
+    lib = _lib.lib()
+    for code, name in _lib.STATUS.items():
+        assert lib.moe_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.moe_status_string(99)
+
+
+def _shape(T=64, d=128, E=8, k=2, F=256, C=0, dt=1):
+    return MoeShape(T, d, E, k, F, C, dt)
+
+
+def _query(s):
+    out = MoeSizes()
+    st = _lib.lib().moe_query(ctypes.byref(s), ctypes.byref(out))
+    return st, out
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_query_sizes_match_definition(name):
+    wl = WORKLOADS[name]
+    s = _shape(wl.T, wl.d, wl.E, wl.k, wl.F, wl.capacity, 1 if wl.dtype == "bf16" else 0)
+    st, q = _query(s)
+    assert st == 0
+    assert q.rows == O.row_space(wl.T, wl.k, wl.E, wl.capacity)
+    assert q.tile_rows in (16, 32, 64, 128)
+    for p in (0, 1):
+        assert q.max_tiles >= O.max_tiles(wl.T, wl.k, wl.E, wl.capacity, q.tile_rows, p)
+    assert q.n_passes == (2 if wl.capacity else 1)
+    eb = 2 if wl.dtype == "bf16" else 4
+    assert q.forward_ws_bytes >= q.rows * (2 * wl.d + wl.F) * eb + q.dispatch_bytes
+
+
+def test_capacity_rows_example():
+    st, q = _query(_shape(T=4096, d=2048, E=64, k=6, F=1408, C=384))
+    assert st == 0 and q.rows == 64 * 384 + (4096 * 6 - 384)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), 1), (dict(E=0), 1), (dict(E=257), 1), (dict(k=0), 1), (dict(k=9, E=8), 1),
+    (dict(k=65, E=100), 1), (dict(C=-1), 1), (dict(dt=7), 1), (dict(d=100), 4), (dict(F=96), 4),
+    (dict(d=32), 1), (dict(T=2**30, k=8), 1),
+])
+def test_query_rejects_bad_shapes(kw, code):
+    st, _ = _query(_shape(**kw))
+    assert st == code
+
+
+def test_null_pointers_rejected_before_gpu():
+    lib = _lib.lib()
+    s = _shape()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_query(None, ctypes.byref(MoeSizes())) == 2
+    assert lib.moe_query(ctypes.byref(s), None) == 2
+    assert lib.moe_route(ctypes.byref(s), None, fake, None, fake, fake, None) == 2
+    assert lib.moe_route(ctypes.byref(s), fake, fake, None, None, fake, None) == 2
+    d = MoeDispatch()
+    assert lib.moe_permute(ctypes.byref(s), fake, fake, ctypes.byref(d), fake, fake, 1 << 20, None) == 2
+    assert lib.moe_permute(ctypes.byref(s), fake, fake, None, fake, fake, 1 << 20, None) == 2
+    assert lib.moe_combine(ctypes.byref(s), fake, fake, None, fake, None) == 2
+    assert lib.moe_forward(ctypes.byref(s), fake, fake, None, None, None, fake, fake, fake, fake, None, 0,
+                           None, None) == 2
+    # ids without weights (or the reverse) is an argument error
+    assert lib.moe_forward(ctypes.byref(s), fake, fake, None, fake, None, fake, fake, fake, fake, fake,
+                           1 << 40, None, None) == 1
+
+
+def test_carve_and_workspace_checks():
+    lib = _lib.lib()
+    s = _shape(T=100, E=16, k=4, C=10)
+    st, q = _query(s)
+    d = MoeDispatch()
+    base = 0x100000
+    assert lib.moe_dispatch_carve(ctypes.byref(s), base, q.dispatch_bytes - 1, ctypes.byref(d)) == 3
+    assert lib.moe_dispatch_carve(ctypes.byref(s), base + 4, q.dispatch_bytes, ctypes.byref(d)) == 1
+    assert lib.moe_dispatch_carve(ctypes.byref(s), base, q.dispatch_bytes, ctypes.byref(d)) == 0
+    ptrs = [getattr(d, n) for n in _lib.DISPATCH_ARRAYS]
+    assert all(p % 256 == 0 and base <= p < base + q.dispatch_bytes for p in ptrs)
+    assert len(set(ptrs)) == len(ptrs)
+    assert d.tile_rows == q.tile_rows and d.max_tiles == q.max_tiles
+    fake = ctypes.c_void_p(0x1000)
+    # permute workspace too small
+    assert lib.moe_permute(ctypes.byref(s), fake, fake, ctypes.byref(d), fake, fake, q.permute_ws_bytes - 1,
+                           None) == 3
+    # forward workspace too small / misaligned
+    assert lib.moe_forward(ctypes.byref(s), fake, fake, None, None, None, fake, fake, fake, fake,
+                           ctypes.c_void_p(0x100000), q.forward_ws_bytes - 1, None, None) == 3
+    assert lib.moe_forward(ctypes.byref(s), fake, fake, None, None, None, fake, fake, fake, fake,
+                           ctypes.c_void_p(0x100010), q.forward_ws_bytes, None, None) == 1
+    # unsupported tile height, undersized tile map
+    d2 = MoeDispatch.from_buffer_copy(d)
+    d2.tile_rows = 48
+    assert lib.moe_ffn_gate_up(ctypes.byref(s), fake, fake, fake, ctypes.byref(d2), 0, fake, None) == 4
+    d2 = MoeDispatch.from_buffer_copy(d)
+    d2.max_tiles = 0
+    assert lib.moe_ffn_down(ctypes.byref(s), fake, fake, ctypes.byref(d2), 0, fake, None) == 1
+    assert lib.moe_ffn_down(ctypes.byref(s), fake, fake, ctypes.byref(d), 2, fake, None) == 1
+
+
+def test_views_struct_layout():
+    # the Python mirror of moe_forward_views_t: a dispatch struct and 5 pointers
+    assert ctypes.sizeof(MoeDispatch) == 10 * 8 + 8
+    assert ctypes.sizeof(MoeForwardViews) == ctypes.sizeof(MoeDispatch) + 5 * 8
+    assert ctypes.sizeof(MoeSizes) == 8 + 4 * 4 + 3 * 8

@@ -1,0 +1,224 @@
+"""GPU parity: every call of libmoe against the CPU oracle on seeded inputs.
+
+Sizes are small enough for the oracle to finish in seconds while spanning
+several row tiles, several column tiles and ragged tails.  Integer outputs
+(ids up to near-ties, counts, offsets, permutation, tile map) must be
+bit-exact; floating-point outputs must satisfy
+max|gpu - oracle| / max|oracle| <= 2e-2 (bf16) or 1e-4 (fp32).
+"""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from tests.gpu_helpers import TOL, bits, check_dispatch, check_routing, dev, host64, rel_err, torch_dtype
+from workloads import get_workload, make_inputs, zipf_routing
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# name, base workload, overrides, routing override
+CASES = {
+    "tiny_f32": ("tiny_f32", {}),
+    "bf16_ragged": ("mixtral_t512", dict(T=200, d=256, F=320)),
+    "bf16_bm128": ("mixtral_t512", dict(T=512, d=128, E=4, F=192)),
+    "bf16_e64_zipf": ("e64_zipf_a1.2", dict(T=96, d=192, F=128)),
+    "bf16_e64_zipf2": ("e64_zipf_a2.0", dict(T=160, d=128, F=192)),
+    "bf16_capacity": ("capacity_gini0.30", dict(T=300, d=128, E=16, k=4, F=192, capacity=40)),
+    "bf16_t1": ("mixtral_t512", dict(T=1, d=256, F=128)),
+    "bf16_dense": ("mixtral_t512", dict(T=50, d=128, E=1, k=1, F=128)),
+    "f32_e256": ("tiny_f32", dict(T=40, d=64, E=256, k=8, F=64)),
+    "f32_capacity": ("tiny_f32", dict(T=64, E=4, k=2, capacity=20)),
+}
+
+
+def _workload(case):
+    base, over = CASES[case]
+    return get_workload(base, **over)
+
+
+def _shape(wl):
+    from grouped_gemm_gemv_amd import Shape
+    return Shape(T=wl.T, d=wl.d, E=wl.E, k=wl.k, F=wl.F, capacity=wl.capacity, dtype=torch_dtype(wl.dtype))
+
+
+class Run:
+    """Inputs on host and device plus every GPU stage, run step by step."""
+
+    def __init__(self, case, seed=0):
+        import grouped_gemm_gemv_amd as M
+        wl = _workload(case)
+        self.wl = wl
+        self.inp = make_inputs(wl, seed)
+        inp = self.inp
+        self.shape = _shape(wl)
+        self.q = M.query(self.shape)
+        dt = torch_dtype(wl.dtype)
+        self.x, self.wr = dev(inp.x), dev(inp.wr)
+        self.wg, self.wu, self.wd = dev(inp.wg), dev(inp.wu), dev(inp.wd)
+        self.bias = dev(inp.bias)
+        T, k = wl.T, wl.k
+        if inp.topk_ids is not None:
+            self.ids = dev(inp.topk_ids)
+            self.w = dev(inp.topk_w)
+            self.logits = None
+        else:
+            self.ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            self.w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+            M.moe_route(self.shape, self.x, self.wr, self.bias, self.ids, self.w)
+            self.logits = O.router_logits(inp.x, inp.wr, wl.dtype, inp.bias)
+        R = self.q.rows
+        self.disp = M.Dispatch(self.shape)
+        self.xp = torch.zeros((R, wl.d), dtype=dt, device="cuda")
+        ws = M.workspace(self.q.permute_ws_bytes)
+        M.moe_permute(self.shape, self.x, self.ids, self.disp, self.xp, ws)
+        self.h = torch.zeros((R, wl.F), dtype=dt, device="cuda")
+        self.y = torch.zeros((R, wl.d), dtype=dt, device="cuda")
+        M.moe_grouped_ffn(self.shape, self.xp, self.wg, self.wu, self.wd, self.disp, self.h, self.y)
+        self.out = torch.empty((T, wl.d), dtype=dt, device="cuda")
+        M.moe_combine(self.shape, self.y, self.w, self.disp, self.out)
+        torch.cuda.synchronize()
+        self.gpu_ids = self.ids.cpu().numpy()
+        self.gpu_w = self.w.cpu().numpy().astype(np.float64)
+        self.ref_disp = O.dispatch(self.gpu_ids, wl.E, wl.capacity, self.q.tile_rows)
+
+
+@pytest.fixture(scope="module")
+def runs():
+    _need_gpu()
+    cache = {}
+
+    def get(case):
+        if case not in cache:
+            print(f"\n[gpu parity] case {case}", flush=True)
+            cache[case] = Run(case)
+        return cache[case]
+    return get
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_route(runs, case):
+    r = runs(case)
+    if r.logits is None:
+        pytest.skip("routing supplied (Zipf ids)")
+    differ = check_routing(r.gpu_ids, r.gpu_w, r.logits, r.wl.k)
+    assert differ <= max(1, r.wl.T // 100)
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_dispatch_bit_exact(runs, case):
+    r = runs(case)
+    check_dispatch(r.disp.arrays(), r.ref_disp, r.wl.E)
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_gather_bitwise(runs, case):
+    r = runs(case)
+    ref = O.gather(r.inp.x, r.ref_disp)
+    live = r.ref_disp["token_of"] >= 0
+    assert np.array_equal(bits(r.xp)[live], ref[live].view(bits(r.xp).dtype))
+
+
+def _oracle_rows(r):
+    """Oracle h and y for every live row (float64)."""
+    wl, inp, d = r.wl, r.inp, r.ref_disp
+    x64 = O.to_f64(inp.x, wl.dtype)
+    h = np.zeros((d["R"], wl.F))
+    y = np.zeros((d["R"], wl.d))
+    ids = r.gpu_ids.reshape(-1)
+    for e in range(wl.E):
+        fs = np.nonzero(ids == e)[0]
+        if fs.size == 0:
+            continue
+        X = x64[fs // wl.k]
+        G = X @ O.to_f64(inp.wg[e], wl.dtype).T
+        U = X @ O.to_f64(inp.wu[e], wl.dtype).T
+        H = O.silu(G) * U
+        rows = d["row_of"][fs]
+        h[rows] = H
+        y[rows] = H @ O.to_f64(inp.wd[e], wl.dtype).T
+    return h, y
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_grouped_ffn(runs, case):
+    r = runs(case)
+    h_ref, y_ref = _oracle_rows(r)
+    live = r.ref_disp["token_of"] >= 0
+    tol = TOL[r.wl.dtype]
+    assert rel_err(host64(r.h)[live], h_ref[live]) <= tol
+    assert rel_err(host64(r.y)[live], y_ref[live]) <= tol
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_layer_output(runs, case):
+    r = runs(case)
+    wl, inp = r.wl, r.inp
+    w_ref = r.gpu_w if r.logits is None else None
+    if w_ref is None:
+        m = r.logits.max(axis=1, keepdims=True)
+        p = np.exp(r.logits - m)
+        sel = np.take_along_axis(p, r.gpu_ids.astype(np.int64), axis=1)
+        w_ref = sel / sel.sum(axis=1, keepdims=True)
+    ref = O.forward(inp.x, inp.wr, inp.wg, inp.wu, inp.wd, wl.k, wl.dtype, topk_ids=r.gpu_ids,
+                    topk_w=w_ref, capacity=wl.capacity, tile_rows=r.q.tile_rows)
+    err = rel_err(host64(r.out), ref["out"])
+    print(f"[{case}] layer rel err {err:.3e}")
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_forward_matches_steps_and_is_deterministic(runs, case):
+    import grouped_gemm_gemv_amd as M
+    r = runs(case)
+    ws = M.workspace(r.q.forward_ws_bytes)
+    supplied = r.logits is None
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(r.out)
+        v = M.moe_forward(r.shape, r.x, r.wr, r.bias, r.ids if supplied else None, r.w if supplied else None,
+                          r.wg, r.wu, r.wd, out, ws)
+        torch.cuda.synchronize()
+        outs.append(bits(out))
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0], bits(r.out))
+    assert np.array_equal(v.topk_ids.cpu().numpy(), r.gpu_ids)
+
+
+@pytest.mark.parametrize("case", ["bf16_capacity", "f32_capacity"])
+def test_capacity_equals_uncapped(runs, case):
+    import grouped_gemm_gemv_amd as M
+    r = runs(case)
+    assert r.ref_disp["spill_counts"].sum() > 0, "case must overflow"
+    shape0 = dataclasses.replace(r.shape, capacity=0)
+    q0 = M.query(shape0)
+    ws = M.workspace(q0.forward_ws_bytes)
+    out0 = torch.empty_like(r.out)
+    M.moe_forward(shape0, r.x, r.wr, r.bias, r.ids, r.w, r.wg, r.wu, r.wd, out0, ws)
+    torch.cuda.synchronize()
+    assert rel_err(host64(r.out), host64(out0)) <= TOL[r.wl.dtype]
+    # each (token, expert) row is computed by the same K loop whatever tile holds it
+    assert np.array_equal(bits(r.out), bits(out0))
+
+
+def test_identity_path_returns_input(runs):
+    """moe_permute then moe_combine with y := x_perm returns x (weights sum to 1)."""
+    import grouped_gemm_gemv_amd as M
+    r = runs("bf16_e64_zipf")
+    out = torch.empty_like(r.x)
+    M.moe_combine(r.shape, r.xp, r.w, r.disp, out)
+    torch.cuda.synchronize()
+    x = host64(r.x)
+    err = np.abs(host64(out) - x)
+    # sum_j w_j * x is x * (1 + O(k * 2^-24)); after bf16 rounding at most 1 ulp away
+    assert (err <= np.abs(x) * 2.0 ** -7 + 1e-30).all()
+    assert (err == 0).mean() > 0.99
