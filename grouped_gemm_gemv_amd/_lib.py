@@ -37,7 +37,7 @@ EXPORTED = [
 
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", c_i32), ("d", c_i32), ("E", c_i32), ("k", c_i32), ("F", c_i32),
-                ("capacity", c_i32), ("dtype", c_i32)]
+                ("capacity", c_i32), ("dtype", c_i32), ("tile_rows", c_i32)]
 
 
 class MoeSizes(ctypes.Structure):

@@ -29,9 +29,10 @@ class Shape:
     F: int
     capacity: int = 0
     dtype: torch.dtype = torch.bfloat16
+    tile_rows: int = 0  # 0: the library chooses
 
     def c(self) -> MoeShape:
-        return MoeShape(self.T, self.d, self.E, self.k, self.F, self.capacity, _DT[self.dtype])
+        return MoeShape(self.T, self.d, self.E, self.k, self.F, self.capacity, _DT[self.dtype], self.tile_rows)
 
 
 def _p(t: Optional[torch.Tensor]) -> Optional[int]:

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "grouped_gemm.hip"]
+SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "gemm_bf16_gateup.hip", "gemm_bf16_down.hip",
+           "gemm_f32_gateup.hip", "gemm_f32_down.hip"]
 
 
 def hipcc() -> str:

@@ -17,18 +17,28 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Rows per tile of the grouped GEMMs: the smallest supported height that
-// covers the expected rows of an active expert (T*k spread over
-// min(E, T*k) experts, at most C in the capacity pass), so that the common
-// expert needs one row tile and its weights stream from HBM once.
+// Largest row-tile height of the grouped GEMMs.  A tile holds up to BM rows
+// and only its non-empty 16-row subtiles are computed, so BM is chosen to
+// cover an active expert's rows with one tile (1.25x the mean of T*k spread
+// over min(E, T*k) experts, at most C in the capacity pass): each expert's
+// weights then stream from HBM once.
+constexpr int kTileRows[] = {16, 32, 48, 64, 96, 128, 160, 192};
+
+bool supported_tile_rows(int bm) {
+  for (int v : kTileRows)
+    if (v == bm) return true;
+  return false;
+}
+
 int choose_tile_rows(const moe_shape_t& s) {
+  if (s.tile_rows != 0) return s.tile_rows;
   const int64_t Tk = (int64_t)s.T * s.k;
   int64_t mean = ceil_div(Tk, std::min<int64_t>(s.E, Tk));
   if (s.capacity > 0) mean = std::min<int64_t>(mean, s.capacity);
-  if (mean <= 16) return 16;
-  if (mean <= 32) return 32;
-  if (mean <= 64) return 64;
-  return 128;
+  const int64_t want = std::max<int64_t>(mean, (mean * 5 + 3) / 4);
+  for (int v : kTileRows)
+    if (v >= want) return v;
+  return kTileRows[sizeof(kTileRows) / sizeof(kTileRows[0]) - 1];
 }
 
 int64_t spill_bound(const moe_shape_t& s) { return std::max<int64_t>(0, (int64_t)s.T * s.k - s.capacity); }
@@ -63,6 +73,7 @@ moe_status_t validate(const moe_shape_t* s) {
       s->d < 64 || s->F < 64)
     return MOE_ERR_INVALID_ARG;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->tile_rows != 0 && !supported_tile_rows(s->tile_rows)) return MOE_ERR_UNSUPPORTED;
   if (s->d % 64 != 0 || s->F % 64 != 0) return MOE_ERR_UNSUPPORTED;
   const int64_t Tk = (int64_t)s->T * s->k;
   if (Tk >= INT32_MAX) return MOE_ERR_INVALID_ARG;
@@ -151,8 +162,7 @@ moe_status_t check_dispatch(const moe_shape_t& s, const Plan& p, const moe_dispa
   if (!d->counts || !d->offsets || !d->spill_counts || !d->spill_offsets || !d->row_of || !d->token_of ||
       !d->tile_off || !d->tile_map || !d->n_tiles || !d->err_flags)
     return MOE_ERR_NULL_PTR;
-  if (d->tile_rows != 16 && d->tile_rows != 32 && d->tile_rows != 64 && d->tile_rows != 128)
-    return MOE_ERR_UNSUPPORTED;
+  if (!supported_tile_rows(d->tile_rows)) return MOE_ERR_UNSUPPORTED;
   const int64_t need = std::max(pass_max_tiles(s, d->tile_rows, 0), pass_max_tiles(s, d->tile_rows, 1));
   if (d->max_tiles < need || d->max_tiles < 1) return MOE_ERR_INVALID_ARG;
   (void)p;

@@ -1,0 +1,42 @@
+// Tile shapes of the grouped GEMMs, per maximum row-tile height BM.
+//
+// WTN: weight rows per wavefront (per projection); WN x WK wavefronts per
+// workgroup (WN split the weight rows, WK split K); PF: iterations of weight
+// prefetch held in registers.  Small BM (decode-sized batches) splits K
+// inside the workgroup so that narrow column tiles still give every CU work
+// and enough bytes in flight; large BM gives each wavefront all rows of the
+// tile so every weight byte feeds BM/16 MFMAs straight from registers.
+#pragma once
+
+namespace moe {
+
+template <int BM_, int WTN_, int WN_, int WK_, int PF_, int WAUX_ = 0>
+struct TileShape {
+  static constexpr int BM = BM_, WTN = WTN_, WN = WN_, WK = WK_, PF = PF_;
+  static constexpr int WAUX = WAUX_;  // cache-policy bits of the weight loads
+};
+
+template <int BM, bool GATED>
+struct TileCfg;
+
+// gate+up (two projections per wavefront)
+template <> struct TileCfg<16, true> { using type = TileShape<16, 32, 1, 4, 2>; };
+template <> struct TileCfg<32, true> { using type = TileShape<32, 32, 1, 4, 2>; };
+template <> struct TileCfg<48, true> { using type = TileShape<48, 32, 2, 2, 2>; };
+template <> struct TileCfg<64, true> { using type = TileShape<64, 32, 2, 2, 2>; };
+template <> struct TileCfg<96, true> { using type = TileShape<96, 32, 4, 1, 2>; };
+template <> struct TileCfg<128, true> { using type = TileShape<128, 32, 4, 1, 2>; };
+template <> struct TileCfg<160, true> { using type = TileShape<160, 32, 4, 1, 2>; };
+template <> struct TileCfg<192, true> { using type = TileShape<192, 32, 4, 1, 2>; };
+
+// down projection
+template <> struct TileCfg<16, false> { using type = TileShape<16, 32, 1, 4, 4>; };
+template <> struct TileCfg<32, false> { using type = TileShape<32, 32, 1, 4, 4>; };
+template <> struct TileCfg<48, false> { using type = TileShape<48, 32, 2, 2, 4>; };
+template <> struct TileCfg<64, false> { using type = TileShape<64, 32, 2, 2, 4>; };
+template <> struct TileCfg<96, false> { using type = TileShape<96, 32, 4, 1, 4>; };
+template <> struct TileCfg<128, false> { using type = TileShape<128, 32, 4, 1, 4>; };
+template <> struct TileCfg<160, false> { using type = TileShape<160, 32, 4, 1, 4>; };
+template <> struct TileCfg<192, false> { using type = TileShape<192, 32, 4, 1, 4>; };
+
+}  // namespace moe

@@ -54,14 +54,14 @@ struct GemmArgs {
   int max_tiles;
 };
 
-// Tile shape of the grouped GEMMs for a tile height and problem.
-struct GemmTiling {
-  int BM;       // rows per tile
-  int cols;     // output columns per workgroup
-  int threads;  // workgroup size
-};
-GemmTiling gemm_tiling(int BM, bool gated, int N);
+hipError_t launch_gemm_bf16_gateup(int BM, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_bf16_down(int BM, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_f32_gateup(int BM, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_f32_down(int BM, const GemmArgs& a, hipStream_t stream);
 
-hipError_t launch_grouped_gemm(int dtype, bool gated, int BM, const GemmArgs& a, hipStream_t stream);
+inline hipError_t launch_grouped_gemm(int dtype, bool gated, int BM, const GemmArgs& a, hipStream_t stream) {
+  if (dtype == 1) return gated ? launch_gemm_bf16_gateup(BM, a, stream) : launch_gemm_bf16_down(BM, a, stream);
+  return gated ? launch_gemm_f32_gateup(BM, a, stream) : launch_gemm_f32_down(BM, a, stream);
+}
 
 }  // namespace moe

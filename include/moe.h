@@ -67,6 +67,9 @@ typedef struct moe_shape {
   int32_t F;        /* expert FFN width                        */
   int32_t capacity; /* C, or 0                                 */
   int32_t dtype;    /* moe_dtype_t                             */
+  int32_t tile_rows;/* row-tile height of the grouped GEMMs: 0 lets the
+                       library choose; else one of 16, 32, 48, 64, 96,
+                       128, 160, 192 (others: MOE_ERR_UNSUPPORTED)      */
 } moe_shape_t;
 
 /* Sizes derived from a shape (all host values). */

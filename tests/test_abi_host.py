@@ -41,8 +41,8 @@ def test_status_strings():
     assert b"unknown" in lib.moe_status_string(99)
 
 
-def _shape(T=64, d=128, E=8, k=2, F=256, C=0, dt=1):
-    return MoeShape(T, d, E, k, F, C, dt)
+def _shape(T=64, d=128, E=8, k=2, F=256, C=0, dt=1, bm=0):
+    return MoeShape(T, d, E, k, F, C, dt, bm)
 
 
 def _query(s):
@@ -58,12 +58,20 @@ def test_query_sizes_match_definition(name):
     st, q = _query(s)
     assert st == 0
     assert q.rows == O.row_space(wl.T, wl.k, wl.E, wl.capacity)
-    assert q.tile_rows in (16, 32, 64, 128)
+    assert q.tile_rows in (16, 32, 48, 64, 96, 128, 160, 192)
     for p in (0, 1):
         assert q.max_tiles >= O.max_tiles(wl.T, wl.k, wl.E, wl.capacity, q.tile_rows, p)
     assert q.n_passes == (2 if wl.capacity else 1)
     eb = 2 if wl.dtype == "bf16" else 4
     assert q.forward_ws_bytes >= q.rows * (2 * wl.d + wl.F) * eb + q.dispatch_bytes
+
+
+def test_tile_rows_override():
+    for bm in (16, 32, 48, 64, 96, 128, 160, 192):
+        st, q = _query(_shape(T=300, E=16, k=4, C=40, bm=bm))
+        assert st == 0 and q.tile_rows == bm
+        for p in (0, 1):
+            assert q.max_tiles >= O.max_tiles(300, 4, 16, 40, bm, p)
 
 
 def test_capacity_rows_example():
@@ -74,7 +82,7 @@ def test_capacity_rows_example():
 @pytest.mark.parametrize("kw,code", [
     (dict(T=0), 1), (dict(E=0), 1), (dict(E=257), 1), (dict(k=0), 1), (dict(k=9, E=8), 1),
     (dict(k=65, E=100), 1), (dict(C=-1), 1), (dict(dt=7), 1), (dict(d=100), 4), (dict(F=96), 4),
-    (dict(d=32), 1), (dict(T=2**30, k=8), 1),
+    (dict(d=32), 1), (dict(T=2**30, k=8), 1), (dict(bm=40), 4), (dict(bm=256), 4),
 ])
 def test_query_rejects_bad_shapes(kw, code):
     st, _ = _query(_shape(**kw))
@@ -124,7 +132,7 @@ def test_carve_and_workspace_checks():
                            ctypes.c_void_p(0x100010), q.forward_ws_bytes, None, None) == 1
     # unsupported tile height, undersized tile map
     d2 = MoeDispatch.from_buffer_copy(d)
-    d2.tile_rows = 48
+    d2.tile_rows = 40
     assert lib.moe_ffn_gate_up(ctypes.byref(s), fake, fake, fake, ctypes.byref(d2), 0, fake, None) == 4
     d2 = MoeDispatch.from_buffer_copy(d)
     d2.max_tiles = 0
@@ -135,5 +143,6 @@ def test_carve_and_workspace_checks():
 def test_views_struct_layout():
     # the Python mirror of moe_forward_views_t: a dispatch struct and 5 pointers
     assert ctypes.sizeof(MoeDispatch) == 10 * 8 + 8
+    assert ctypes.sizeof(MoeShape) == 8 * 4
     assert ctypes.sizeof(MoeForwardViews) == ctypes.sizeof(MoeDispatch) + 5 * 8
     assert ctypes.sizeof(MoeSizes) == 8 + 4 * 4 + 3 * 8

@@ -30,7 +30,6 @@ def _need_gpu():
 CASES = {
     "tiny_f32": ("tiny_f32", {}),
     "bf16_ragged": ("mixtral_t512", dict(T=200, d=256, F=320)),
-    "bf16_bm128": ("mixtral_t512", dict(T=512, d=128, E=4, F=192)),
     "bf16_e64_zipf": ("e64_zipf_a1.2", dict(T=96, d=192, F=128)),
     "bf16_e64_zipf2": ("e64_zipf_a2.0", dict(T=160, d=128, F=192)),
     "bf16_capacity": ("capacity_gini0.30", dict(T=300, d=128, E=16, k=4, F=192, capacity=40)),
@@ -38,6 +37,12 @@ CASES = {
     "bf16_dense": ("mixtral_t512", dict(T=50, d=128, E=1, k=1, F=128)),
     "f32_e256": ("tiny_f32", dict(T=40, d=64, E=256, k=8, F=64)),
     "f32_capacity": ("tiny_f32", dict(T=64, E=4, k=2, capacity=20)),
+    # tile heights 48 / 96 / 128 / 160 and column tails (F or d not a multiple of the column tile)
+    "bf16_bm48": ("mixtral_t512", dict(T=152, d=128, F=128)),
+    "bf16_bm96": ("mixtral_t512", dict(T=256, d=128, F=192)),
+    "bf16_bm128": ("mixtral_t512", dict(T=400, d=128, F=256)),
+    "bf16_bm160": ("mixtral_t512", dict(T=512, d=256, F=128)),
+    "bf16_bm192": ("mixtral_t512", dict(T=512, d=128, E=4, F=192)),
 }
 
 
@@ -196,17 +201,21 @@ def test_forward_matches_steps_and_is_deterministic(runs, case):
 
 @pytest.mark.parametrize("case", ["bf16_capacity", "f32_capacity"])
 def test_capacity_equals_uncapped(runs, case):
+    """Capacity + overflow pass gives the uncapped layer output; with the same
+    tile configuration every (token, expert) row runs the same K loop, so the
+    two are bitwise equal."""
     import grouped_gemm_gemv_amd as M
     r = runs(case)
     assert r.ref_disp["spill_counts"].sum() > 0, "case must overflow"
-    shape0 = dataclasses.replace(r.shape, capacity=0)
-    q0 = M.query(shape0)
-    ws = M.workspace(q0.forward_ws_bytes)
-    out0 = torch.empty_like(r.out)
-    M.moe_forward(shape0, r.x, r.wr, r.bias, r.ids, r.w, r.wg, r.wu, r.wd, out0, ws)
-    torch.cuda.synchronize()
-    assert rel_err(host64(r.out), host64(out0)) <= TOL[r.wl.dtype]
-    # each (token, expert) row is computed by the same K loop whatever tile holds it
+    bm = r.q.tile_rows
+    for shape0 in (dataclasses.replace(r.shape, capacity=0),
+                   dataclasses.replace(r.shape, capacity=0, tile_rows=bm)):
+        q0 = M.query(shape0)
+        ws = M.workspace(q0.forward_ws_bytes)
+        out0 = torch.empty_like(r.out)
+        M.moe_forward(shape0, r.x, r.wr, r.bias, r.ids, r.w, r.wg, r.wu, r.wd, out0, ws)
+        torch.cuda.synchronize()
+        assert rel_err(host64(r.out), host64(out0)) <= TOL[r.wl.dtype]
     assert np.array_equal(bits(r.out), bits(out0))
 
 
