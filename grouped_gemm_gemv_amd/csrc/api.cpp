@@ -177,6 +177,29 @@ moe_status_t enqueue_permute(const moe_shape_t& s, const Plan& p, const void* x,
   int32_t* block_counts = reinterpret_cast<int32_t*>(w);
   uint32_t* block_err = reinterpret_cast<uint32_t*>(w + align_up(4 * (size_t)p.nblk * s.E));
   const int Tk = (int)p.Tk;
+  if (Tk <= moe::kSmallDispatch) {
+    moe::SmallDispatchArgs a;
+    a.ids = ids;
+    a.Tk = Tk;
+    a.k = s.k;
+    a.E = s.E;
+    a.C = s.capacity;
+    a.BM = d.tile_rows;
+    a.max_tiles = d.max_tiles;
+    a.rows = p.R;
+    a.counts = d.counts;
+    a.offsets = d.offsets;
+    a.spill_counts = d.spill_counts;
+    a.spill_offsets = d.spill_offsets;
+    a.row_of = d.row_of;
+    a.token_of = d.token_of;
+    a.tile_off = d.tile_off;
+    a.tile_map = d.tile_map;
+    a.n_tiles = d.n_tiles;
+    a.err_flags = d.err_flags;
+    if (moe::launch_dispatch_small(a, st) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(moe::launch_gather(x, d.row_of, Tk, s.k, (int64_t)s.d * elt_bytes(s), x_perm, st));
+  }
   hipError_t e = moe::launch_count(ids, Tk, s.E, p.nblk, block_counts, block_err, d.token_of, p.R, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   moe::ScanArgs a;

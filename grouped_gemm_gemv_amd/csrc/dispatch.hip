@@ -19,8 +19,10 @@
 //   scatter : one block per 2048 entries; stable in-block ranks from
 //             wavefront ballots (a match mask built bit by bit over the
 //             expert id) plus an LDS prefix across wavefronts and rounds.
+//   dispatch_small : all of the above in one 1024-thread block when T*k is
+//             at most kSmallDispatch (one launch instead of three).
 //   gather  : one wavefront per entry, 16-byte vector row copy.
-//   combine : one wavefront per token, fp32 weighted sum in slot order.
+//   combine : one workgroup per token, fp32 weighted sum in slot order.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -54,7 +56,9 @@ __global__ __launch_bounds__(kThreads) void count_kernel(const int32_t* __restri
     token_of[r] = -1;
 }
 
-// Exclusive scan of one int per thread over a 256-thread block.
+// Exclusive scan of one int per thread over a block of NW wavefronts; every
+// thread of the block must call it.  `tmp` holds NW ints of LDS.
+template <int NW>
 __device__ int block_exclusive_scan(int v, int* tmp, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
@@ -66,8 +70,13 @@ __device__ int block_exclusive_scan(int v, int* tmp, int& total) {
   if (lane == 63) tmp[wave] = inc;
   __syncthreads();
   int before = 0;
-  for (int w = 0; w < wave; ++w) before += tmp[w];
-  total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = tmp[w];
+    before += (w < wave) ? t : 0;
+    total += t;
+  }
   __syncthreads();
   return before + inc - v;
 }
@@ -87,12 +96,12 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
     }
   }
   int total;
-  const int off = block_exclusive_scan(ok ? n : 0, tmp, total);
+  const int off = block_exclusive_scan<4>(ok ? n : 0, tmp, total);
   const int C = a.C;
   const int kept = ok ? (C > 0 ? min(n, C) : n) : 0;
   const int spill = ok ? (C > 0 ? max(n - C, 0) : 0) : 0;
   int spill_total;
-  const int spill_off = block_exclusive_scan(spill, tmp, spill_total);
+  const int spill_off = block_exclusive_scan<4>(spill, tmp, spill_total);
   if (ok) {
     a.counts[e] = n;
     a.offsets[e] = off;
@@ -110,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
     const int base = (p == 0) ? (C > 0 ? e * C : off) : a.E * C + spill_off;
     const int tiles = (rows + BM - 1) / BM;
     int ntiles;
-    const int toff = block_exclusive_scan(tiles, tmp, ntiles);
+    const int toff = block_exclusive_scan<4>(tiles, tmp, ntiles);
     int32_t* tile_off = a.tile_off + p * (a.E + 1);
     int32_t* tile_map = a.tile_map + (size_t)p * a.max_tiles * 4;
     if (ok) tile_off[e] = toff;
@@ -219,26 +228,156 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const char* __restric
                                                            int d, char* __restrict__ out) {
   using Elt = typename Tr::T;
   constexpr int EPC = Tr::EPC;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
+  const int t = blockIdx.x;
   const size_t row_bytes = (size_t)d * sizeof(Elt);
   const int nchunk = d / EPC;
-  for (int c = lane; c < nchunk; c += 64) {
+  for (int c = threadIdx.x; c < nchunk; c += kThreads) {
     float acc[EPC];
 #pragma unroll
     for (int i = 0; i < EPC; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int row = row_of[(size_t)t * k + j];
-      if (row < 0) continue;
-      const float wj = topk_w[(size_t)t * k + j];
-      const uint4 ch = *reinterpret_cast<const uint4*>(y + (size_t)row * row_bytes + (size_t)c * 16);
-      float v[EPC];
-      widen<Tr>(ch, v);
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      uint4 ch[4];
+      float wj[4];
+      bool ok[4];
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u;
+        const int row = (j < k) ? row_of[(size_t)t * k + j] : -1;
+        ok[u] = row >= 0;
+        wj[u] = ok[u] ? topk_w[(size_t)t * k + j] : 0.f;
+        ch[u] = ok[u] ? *reinterpret_cast<const uint4*>(y + (size_t)row * row_bytes + (size_t)c * 16)
+                      : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (ok[u]) {
+          float v[EPC];
+          widen<Tr>(ch[u], v);
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) acc[i] = fmaf(wj[u], v[i], acc[i]);
+        }
+      }
     }
     *reinterpret_cast<uint4*>(out + (size_t)t * row_bytes + (size_t)c * 16) = narrow<Tr>(acc);
+  }
+}
+
+// Whole dispatch (count, scans, capacity split, tile map, stable ranks) in
+// one workgroup of 1024 threads, for T*k up to kSmallDispatch: one launch
+// instead of three.  Same results as count + scan + scatter.
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(SmallDispatchArgs a) {
+  constexpr int NW = 16;
+  __shared__ int hist[256];
+  __shared__ int run[256];
+  __shared__ int wcnt[NW][256];
+  __shared__ int tmp[NW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, C = a.C, BM = a.BM;
+  for (int i = tid; i < 256; i += 1024) {
+    hist[i] = 0;
+    run[i] = 0;
+  }
+  for (int i = tid; i < NW * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+  for (int64_t r = tid; r < a.rows; r += 1024) a.token_of[r] = -1;
+  __syncthreads();
+  int bad = 0;
+  for (int f = tid; f < a.Tk; f += 1024) {
+    const int e = a.ids[f];
+    if ((unsigned)e < (unsigned)E)
+      atomicAdd(&hist[e], 1);
+    else
+      bad = 1;
+  }
+  bad = __syncthreads_or(bad);
+  const bool ok = tid < E;
+  const int n = ok ? hist[tid] : 0;
+  int total;
+  const int off = block_exclusive_scan<NW>(n, tmp, total);
+  const int kept = ok ? (C > 0 ? min(n, C) : n) : 0;
+  const int spill = ok ? (C > 0 ? max(n - C, 0) : 0) : 0;
+  int spill_total;
+  const int spill_off = block_exclusive_scan<NW>(spill, tmp, spill_total);
+  if (ok) {
+    a.counts[tid] = n;
+    a.offsets[tid] = off;
+    a.spill_counts[tid] = spill;
+    a.spill_offsets[tid] = spill_off;
+    hist[tid] = off;          // now: first row of expert tid (uncapped)
+    run[tid] = spill_off;     // now: first overflow row of expert tid, relative to E*C
+  }
+  if (tid == 0) {
+    a.offsets[E] = total;
+    a.spill_offsets[E] = spill_total;
+    a.err_flags[0] = bad ? 1u : 0u;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int rows = (p == 0) ? kept : spill;
+    const int base = (p == 0) ? (C > 0 ? tid * C : off) : E * C + spill_off;
+    const int tiles = (rows + BM - 1) / BM;
+    int ntiles;
+    const int toff = block_exclusive_scan<NW>(tiles, tmp, ntiles);
+    int32_t* tile_off = a.tile_off + p * (E + 1);
+    int32_t* tile_map = a.tile_map + (size_t)p * a.max_tiles * 4;
+    if (ok) tile_off[tid] = toff;
+    if (tid == 0) {
+      tile_off[E] = ntiles;
+      a.n_tiles[p] = ntiles;
+    }
+    for (int i = 0; i < tiles; ++i) {
+      int4 ent;
+      ent.x = tid;
+      ent.y = base + i * BM;
+      ent.z = min(BM, rows - i * BM);
+      ent.w = i;
+      reinterpret_cast<int4*>(tile_map)[toff + i] = ent;
+    }
+  }
+  // stable ranks: rounds of 1024 entries in ascending f
+  __shared__ int rank_base[256];
+  for (int i = tid; i < 256; i += 1024) rank_base[i] = 0;
+  __syncthreads();
+  const int nbits = (E <= 1) ? 0 : 32 - __clz(E - 1);
+  const uint64_t lt = lanemask_lt(lane);
+  for (int f0 = 0; f0 < a.Tk; f0 += 1024) {
+    const int f = f0 + tid;
+    const bool valid = f < a.Tk;
+    const int e = valid ? a.ids[f] : -1;
+    const bool eok = valid && (unsigned)e < (unsigned)E;
+    uint64_t m = __ballot(eok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = eok && ((e >> b) & 1);
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const int lrank = __popcll(m & lt);
+    if (eok && lrank == 0) wcnt[wave][e] = __popcll(m);
+    __syncthreads();
+    if (eok) {
+      int g = rank_base[e] + lrank;
+      for (int w = 0; w < wave; ++w) g += wcnt[w][e];
+      int row;
+      if (C > 0)
+        row = (g < C) ? e * C + g : E * C + run[e] + (g - C);
+      else
+        row = hist[e] + g;
+      a.row_of[f] = row;
+      a.token_of[row] = f / a.k;
+    } else if (valid) {
+      a.row_of[f] = -1;
+    }
+    __syncthreads();
+    for (int i = tid; i < E; i += 1024) {
+      int sum = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        sum += wcnt[w][i];
+        wcnt[w][i] = 0;
+      }
+      rank_base[i] += sum;
+    }
+    __syncthreads();
   }
 }
 
@@ -271,9 +410,14 @@ hipError_t launch_gather(const void* x, const int32_t* row_of, int Tk, int k, in
   return hipGetLastError();
 }
 
+hipError_t launch_dispatch_small(const SmallDispatchArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(int dtype, const void* y, const float* topk_w, const int32_t* row_of, int T,
                           int k, int d, void* out, hipStream_t stream) {
-  const dim3 grid((T + 3) / 4), block(kThreads);
+  const dim3 grid(T), block(kThreads);
   if (dtype == 1)
     hipLaunchKernelGGL(combine_kernel<TBF16>, grid, block, 0, stream, static_cast<const char*>(y), topk_w, row_of, T,
                        k, d, static_cast<char*>(out));

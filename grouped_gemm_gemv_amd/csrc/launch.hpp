@@ -32,6 +32,26 @@ struct ScanArgs {
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 
+// Entries up to which one 1024-thread block does the whole dispatch.
+constexpr int kSmallDispatch = 16384;
+
+struct SmallDispatchArgs {
+  const int32_t* ids;
+  int Tk, k, E, C, BM, max_tiles;
+  int64_t rows;  // R: every row's token_of is reset to -1 first
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* spill_counts;
+  int32_t* spill_offsets;
+  int32_t* row_of;
+  int32_t* token_of;
+  int32_t* tile_off;
+  int32_t* tile_map;
+  int32_t* n_tiles;
+  uint32_t* err_flags;
+};
+hipError_t launch_dispatch_small(const SmallDispatchArgs& a, hipStream_t stream);
+
 hipError_t launch_scatter(const int32_t* ids, int Tk, int k, int E, int C, int nblk,
                           const int32_t* block_base, const int32_t* offsets, const int32_t* spill_offsets,
                           int32_t* row_of, int32_t* token_of, hipStream_t stream);

@@ -8,12 +8,13 @@
 // softmax denominator cancels in the renormalisation, the kept weights are
 // exp(l_j - l_max) / sum_{kept} exp(l_j' - l_max).
 //
-// One workgroup (4 wavefronts) handles 16 tokens.  The 16 x E logit tile is
-// a small NT GEMM on the matrix cores (experts as MFMA rows, tokens as
-// columns), with the four wavefronts splitting K and adding their partial
-// tiles in a fixed order through LDS.  Top-k is then k rounds of a
-// wavefront-wide (value, index) argmax with cross-lane shuffles; a
-// wavefront handles one token at a time with one expert per lane (E <= 256
+// One workgroup handles 16 tokens.  The 16 x E logit tile is a small NT GEMM
+// on the matrix cores (experts as MFMA rows, tokens as columns).  KW
+// wavefronts split K (64-byte slabs, wavefront w takes slabs w, w+KW, ...),
+// each issuing all loads of U slabs before its MFMAs; the KW partial tiles
+// are added in a fixed order through LDS (bitwise reproducible).  Top-k is
+// then k rounds of a wavefront-wide (value, index) argmax with cross-lane
+// shuffles, one token per wavefront at a time, one expert per lane (E <= 256
 // gives up to 4 per lane).
 #include <float.h>
 
@@ -25,90 +26,80 @@ namespace {
 
 constexpr int kTok = kRouteTokens;
 
-template <class Tr>
-__global__ __launch_bounds__(256) void route_kernel(const typename Tr::T* __restrict__ x,
-                                                    const typename Tr::T* __restrict__ wr,
-                                                    const float* __restrict__ bias, int T, int d, int E,
-                                                    int k, int32_t* __restrict__ topk_ids,
-                                                    float* __restrict__ topk_w) {
+// NS: 16-expert subtiles (E <= 16*NS); KW: wavefronts splitting K; U: slabs per wavefront per round.
+template <class Tr, int NS, int KW, int U>
+__global__ __launch_bounds__(64 * KW) void route_kernel(const typename Tr::T* __restrict__ x,
+                                                        const typename Tr::T* __restrict__ wr,
+                                                        const float* __restrict__ bias, int T, int d, int E,
+                                                        int k, int32_t* __restrict__ topk_ids,
+                                                        float* __restrict__ topk_w) {
   using Elt = typename Tr::T;
-  extern __shared__ float route_lds[];
-  const int E16 = (E + 15) & ~15;
-  float* part = route_lds;                  // [3][E16][kTok]  partials of waves 1..3
-  float* logit = route_lds + 3 * E16 * kTok;  // [kTok][E16]
+  constexpr int E16 = NS * 16;
+  __shared__ float part[KW][E16][kTok];  // per-wavefront partial logits
+  __shared__ float logit[kTok][E16];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kTok;
-  const int nsub = E16 / 16;
-  const int tok = t0 + (lane & 15);
-  const size_t row_bytes = (size_t)d * sizeof(Elt);
-  const char* xrow = reinterpret_cast<const char*>(x) + (size_t)(tok < T ? tok : 0) * row_bytes;
-  const bool tok_ok = tok < T;
-  const int nslab = (int)(row_bytes / 64);
-  const int koff = (lane >> 4) * 16;
+  const int ntok = min(kTok, T - t0);
+  const int row_bytes = d * (int)sizeof(Elt);
+  const int nslab = row_bytes / 64;
+  // tokens past T and experts past E read as zero (buffer bounds)
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<Elt*>(x + (size_t)t0 * d), (short)0, ntok * row_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<Elt*>(wr), (short)0, E * row_bytes, 0x00020000);
+  const int xoff = (lane & 15) * row_bytes + (lane >> 4) * 16;
 
-  f32x4_t acc[16];
+  f32x4_t acc[NS];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NS; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int s = wave; s < nslab; s += 4) {
-    const size_t off = (size_t)s * 64 + koff;
-    uint4 a = make_uint4(0, 0, 0, 0);
-    if (tok_ok) a = *reinterpret_cast<const uint4*>(xrow + off);
+  for (int base = 0; base < nslab; base += KW * U) {
+    uint4 xa[U];
+    uint4 wa[U][NS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < nsub) {
-        const int e = i * 16 + (lane & 15);
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (e < E) w = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(wr) + (size_t)e * row_bytes + off);
-        acc[i] = mma16<Tr>(w, a, acc[i]);
+    for (int u = 0; u < U; ++u) {
+      const int s = min(base + u * KW + wave, nslab - 1);
+      xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, s * 64, 0));
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        wa[u][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrr, xoff + i * 16 * row_bytes, s * 64, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (base + u * KW + wave < nslab) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) acc[i] = mma16<Tr>(wa[u][i], xa[u], acc[i]);
       }
     }
   }
   // acc[i][r] = partial logit of expert 16*i + 4*(lane/16) + r for token lane%16
-  if (wave > 0) {
-    float* p = part + (size_t)(wave - 1) * E16 * kTok;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < nsub) {
+  for (int i = 0; i < NS; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[(i * 16 + (lane >> 4) * 4 + r) * kTok + (lane & 15)] = acc[i][r];
-      }
-    }
-  }
+    for (int r = 0; r < 4; ++r) part[wave][i * 16 + (lane >> 4) * 4 + r][lane & 15] = acc[i][r];
   __syncthreads();
-  if (wave == 0) {
+  for (int idx = threadIdx.x; idx < E16 * kTok; idx += 64 * KW) {
+    const int e = idx / kTok, t = idx - e * kTok;
+    float v = part[0][e][t];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < nsub) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = i * 16 + (lane >> 4) * 4 + r;
-          const int idx = e * kTok + (lane & 15);
-          float v = acc[i][r];
-          v += part[idx];
-          v += part[E16 * kTok + idx];
-          v += part[2 * E16 * kTok + idx];
-          if (bias != nullptr && e < E) v += bias[e];
-          logit[(lane & 15) * E16 + e] = v;
-        }
-      }
-    }
+    for (int w = 1; w < KW; ++w) v += part[w][e][t];
+    if (bias != nullptr && e < E) v += bias[e];
+    logit[t][e] = v;
   }
   __syncthreads();
 
-  // top-k: wave w takes tokens 4w .. 4w+3 of the block
-  for (int tt = wave * 4; tt < wave * 4 + 4; ++tt) {
+  // top-k: wavefront w takes tokens w, w + KW, ...
+  for (int tt = wave; tt < ntok; tt += KW) {
     const int t = t0 + tt;
-    if (t >= T) break;
     float v[4];
-    bool taken[4];
+    unsigned taken = 0;  // bit q: expert lane + 64 q is chosen or absent
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane + 64 * q;
-      v[q] = (e < E) ? logit[tt * E16 + e] : -FLT_MAX;
-      taken[q] = !(e < E);
+      v[q] = (e < E) ? logit[tt][e] : -FLT_MAX;
+      if (!(e < E)) taken |= 1u << q;
     }
     int my_id = 0;
     float my_val = 0.f;
@@ -118,7 +109,7 @@ __global__ __launch_bounds__(256) void route_kernel(const typename Tr::T* __rest
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
-        if (!taken[q] && (bi == 0x7fffffff || v[q] > bv)) {
+        if (!((taken >> q) & 1u) && (bi == 0x7fffffff || v[q] > bv)) {
           bv = v[q];
           bi = e;
         }
@@ -132,7 +123,7 @@ __global__ __launch_bounds__(256) void route_kernel(const typename Tr::T* __rest
           bi = oi;
         }
       }
-      if ((bi & 63) == lane) taken[bi >> 6] = true;
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
       if (lane == j) {
         my_id = bi;
         my_val = bv;
@@ -150,22 +141,32 @@ __global__ __launch_bounds__(256) void route_kernel(const typename Tr::T* __rest
   }
 }
 
+template <class Tr>
+hipError_t launch_t(const void* x, const void* w_router, const float* bias, int T, int d, int E, int k,
+                    int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  using Elt = typename Tr::T;
+  const dim3 grid((T + kTok - 1) / kTok);
+  const Elt* xp = static_cast<const Elt*>(x);
+  const Elt* wp = static_cast<const Elt*>(w_router);
+  if (E <= 16)
+    hipLaunchKernelGGL((route_kernel<Tr, 1, 16, 8>), grid, dim3(1024), 0, stream, xp, wp, bias, T, d, E, k, topk_ids, topk_w);
+  else if (E <= 32)
+    hipLaunchKernelGGL((route_kernel<Tr, 2, 16, 8>), grid, dim3(1024), 0, stream, xp, wp, bias, T, d, E, k, topk_ids, topk_w);
+  else if (E <= 64)
+    hipLaunchKernelGGL((route_kernel<Tr, 4, 16, 4>), grid, dim3(1024), 0, stream, xp, wp, bias, T, d, E, k, topk_ids, topk_w);
+  else if (E <= 128)
+    hipLaunchKernelGGL((route_kernel<Tr, 8, 8, 2>), grid, dim3(512), 0, stream, xp, wp, bias, T, d, E, k, topk_ids, topk_w);
+  else
+    hipLaunchKernelGGL((route_kernel<Tr, 16, 4, 2>), grid, dim3(256), 0, stream, xp, wp, bias, T, d, E, k, topk_ids, topk_w);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* bias, int T, int d,
                         int E, int k, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
-  const int E16 = (E + 15) & ~15;
-  const size_t lds = (size_t)(3 * E16 * kTok + kTok * E16) * sizeof(float);
-  const dim3 grid((T + kTok - 1) / kTok), block(256);
-  if (dtype == 1) {
-    hipLaunchKernelGGL(route_kernel<TBF16>, grid, block, lds, stream,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), bias, T, d, E,
-                       k, topk_ids, topk_w);
-  } else {
-    hipLaunchKernelGGL(route_kernel<TF32>, grid, block, lds, stream, static_cast<const float*>(x),
-                       static_cast<const float*>(w_router), bias, T, d, E, k, topk_ids, topk_w);
-  }
-  return hipGetLastError();
+  if (dtype == 1) return launch_t<TBF16>(x, w_router, bias, T, d, E, k, topk_ids, topk_w, stream);
+  return launch_t<TF32>(x, w_router, bias, T, d, E, k, topk_ids, topk_w, stream);
 }
 
 }  // namespace moe

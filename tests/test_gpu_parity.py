@@ -231,3 +231,83 @@ def test_identity_path_returns_input(runs):
     # sum_j w_j * x is x * (1 + O(k * 2^-24)); after bf16 rounding at most 1 ulp away
     assert (err <= np.abs(x) * 2.0 ** -7 + 1e-30).all()
     assert (err == 0).mean() > 0.99
+
+
+@pytest.mark.parametrize("E,k,dt", [(24, 3, "bf16"), (64, 8, "bf16"), (100, 6, "f32"), (128, 16, "bf16"),
+                                    (256, 64, "bf16"), (5, 5, "f32")])
+def test_route_every_expert_range(E, k, dt):
+    """Router kernels for E <= 16, 32, 64, 128, 256 (one instantiation each), k up to 64 and k = E."""
+    _need_gpu()
+    import grouped_gemm_gemv_amd as M
+    base = "tiny_f32" if dt == "f32" else "mixtral_t512"
+    wl = get_workload(base, T=70, d=320, E=E, k=k, F=64, wr_std=0.5 if dt == "bf16" else 1.0)
+    inp = make_inputs(wl, 3, experts=False)
+    shape = _shape(wl)
+    ids = torch.empty((wl.T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((wl.T, k), dtype=torch.float32, device="cuda")
+    print(f"\n[gpu parity] route E={E} k={k} {dt}", flush=True)
+    M.moe_route(shape, dev(inp.x), dev(inp.wr), None, ids, w)
+    torch.cuda.synchronize()
+    logits = O.router_logits(inp.x, inp.wr, wl.dtype)
+    differ = check_routing(ids.cpu().numpy(), w.cpu().numpy().astype(np.float64), logits, k)
+    assert differ <= 1
+
+
+@pytest.mark.parametrize("C", [0, 200])
+def test_dispatch_multiblock_path(C):
+    """T*k above the single-workgroup limit: count + scan + scatter kernels."""
+    _need_gpu()
+    import grouped_gemm_gemv_amd as M
+    T, k, E = 5000, 4, 64
+    rng = np.random.default_rng(7)
+    # skewed ids, distinct per token
+    p = np.arange(1, E + 1, dtype=np.float64) ** -1.0
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+    shape = M.Shape(T=T, d=64, E=E, k=k, F=64, capacity=C, dtype=torch.bfloat16)
+    q = M.query(shape)
+    x = torch.randn((T, 64), device="cuda").to(torch.bfloat16)
+    disp = M.Dispatch(shape)
+    xp = torch.zeros((q.rows, 64), dtype=torch.bfloat16, device="cuda")
+    print(f"\n[gpu parity] multiblock dispatch C={C}", flush=True)
+    M.moe_permute(shape, x, dev(ids), disp, xp, M.workspace(q.permute_ws_bytes))
+    torch.cuda.synchronize()
+    ref = O.dispatch(ids, E, C, q.tile_rows)
+    if C:
+        assert ref["spill_counts"].sum() > 0
+    check_dispatch(disp.arrays(), ref, E)
+    xb = bits(x)
+    live = ref["token_of"] >= 0
+    assert np.array_equal(bits(xp)[live], xb[ref["token_of"][live]])
+
+
+def test_invalid_ids_flagged_and_skipped():
+    """Ids outside [0, E) set err_flags bit 0, get row -1 and contribute nothing."""
+    _need_gpu()
+    import grouped_gemm_gemv_amd as M
+    T, k, E = 40, 2, 8
+    rng = np.random.default_rng(8)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[3, 1] = E
+    ids[17, 0] = -1
+    shape = M.Shape(T=T, d=64, E=E, k=k, F=64, dtype=torch.bfloat16)
+    q = M.query(shape)
+    x = torch.randn((T, 64), device="cuda").to(torch.bfloat16)
+    disp = M.Dispatch(shape)
+    xp = torch.zeros((q.rows, 64), dtype=torch.bfloat16, device="cuda")
+    M.moe_permute(shape, x, dev(ids), disp, xp, M.workspace(q.permute_ws_bytes))
+    torch.cuda.synchronize()
+    a = disp.arrays()
+    assert int(a["err_flags"].cpu()[0]) & 1
+    row_of = a["row_of"].cpu().numpy()
+    assert row_of[3 * k + 1] == -1 and row_of[17 * k + 0] == -1
+    valid = np.ones(T * k, bool)
+    valid[[3 * k + 1, 17 * k]] = False
+    assert a["counts"].cpu().numpy().sum() == valid.sum()
+    # the identity combine of the valid slots: weight 1 on each valid slot
+    w = torch.zeros((T, k), dtype=torch.float32, device="cuda")
+    w[:, 0] = 1.0
+    w[17, 1] = 1.0
+    out = torch.empty_like(x)
+    M.moe_combine(shape, xp, w, disp, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(x))
