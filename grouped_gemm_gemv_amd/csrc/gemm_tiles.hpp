@@ -20,23 +20,23 @@ template <int BM, bool GATED>
 struct TileCfg;
 
 // gate+up (two projections per wavefront)
-template <> struct TileCfg<16, true> { using type = TileShape<16, 32, 1, 4, 2>; };
-template <> struct TileCfg<32, true> { using type = TileShape<32, 32, 1, 4, 2>; };
-template <> struct TileCfg<48, true> { using type = TileShape<48, 32, 2, 2, 2>; };
-template <> struct TileCfg<64, true> { using type = TileShape<64, 32, 2, 2, 2>; };
-template <> struct TileCfg<96, true> { using type = TileShape<96, 32, 4, 1, 2>; };
-template <> struct TileCfg<128, true> { using type = TileShape<128, 32, 4, 1, 2>; };
-template <> struct TileCfg<160, true> { using type = TileShape<160, 32, 4, 1, 2>; };
-template <> struct TileCfg<192, true> { using type = TileShape<192, 32, 4, 1, 2>; };
+template <> struct TileCfg<16, true> { using type = TileShape<16, 32, 1, 4, 4>; };
+template <> struct TileCfg<32, true> { using type = TileShape<32, 32, 1, 4, 4>; };
+template <> struct TileCfg<48, true> { using type = TileShape<48, 32, 2, 2, 4>; };
+template <> struct TileCfg<64, true> { using type = TileShape<64, 32, 2, 2, 4>; };
+template <> struct TileCfg<96, true> { using type = TileShape<96, 16, 8, 1, 4>; };
+template <> struct TileCfg<128, true> { using type = TileShape<128, 16, 8, 1, 4>; };
+template <> struct TileCfg<160, true> { using type = TileShape<160, 16, 8, 1, 4>; };
+template <> struct TileCfg<192, true> { using type = TileShape<192, 16, 8, 1, 4>; };
 
 // down projection
 template <> struct TileCfg<16, false> { using type = TileShape<16, 32, 1, 4, 4>; };
 template <> struct TileCfg<32, false> { using type = TileShape<32, 32, 1, 4, 4>; };
 template <> struct TileCfg<48, false> { using type = TileShape<48, 32, 2, 2, 4>; };
 template <> struct TileCfg<64, false> { using type = TileShape<64, 32, 2, 2, 4>; };
-template <> struct TileCfg<96, false> { using type = TileShape<96, 32, 4, 1, 4>; };
-template <> struct TileCfg<128, false> { using type = TileShape<128, 32, 4, 1, 4>; };
-template <> struct TileCfg<160, false> { using type = TileShape<160, 32, 4, 1, 4>; };
-template <> struct TileCfg<192, false> { using type = TileShape<192, 32, 4, 1, 4>; };
+template <> struct TileCfg<96, false> { using type = TileShape<96, 16, 8, 1, 4>; };
+template <> struct TileCfg<128, false> { using type = TileShape<128, 16, 8, 1, 4>; };
+template <> struct TileCfg<160, false> { using type = TileShape<160, 16, 8, 1, 4>; };
+template <> struct TileCfg<192, false> { using type = TileShape<192, 16, 8, 1, 4>; };
 
 }  // namespace moe

@@ -27,8 +27,8 @@
 //
 // Data movement per iteration (WK steps):
 //  - the activation tile (MS*16 rows x WK*128 bytes) is loaded by the whole
-//    workgroup two iterations ahead into registers and written into a
-//    double-buffered LDS tile (rows padded by 16 bytes so 16-byte lane reads
+//    workgroup two iterations ahead into registers and written, one
+//    iteration ahead, into a double-buffered LDS tile (rows padded by 16 bytes so 16-byte lane reads
 //    of 16 consecutive rows hit distinct banks); rows past the tile's last
 //    row read as zeros;
 //  - weights are streamed by each wavefront straight into MFMA operand
@@ -53,6 +53,8 @@
 // and the activation rows of one expert stay in that XCD's L2.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "gemm_tiles.hpp"
 #include "launch.hpp"
@@ -61,6 +63,15 @@ namespace moe {
 namespace gemm {
 
 constexpr int kKB = 128;  // bytes of K per step
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time unroll).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
@@ -73,37 +84,64 @@ struct Gemm {
   static constexpr int MSUB = BM / 16;
   static constexpr int WL = NMAT * NSUB * 2;      // 16-byte weight loads per lane per step
   static constexpr int ROWB = WK * kKB;           // activation bytes per row per iteration
-  static constexpr int STRIDE = ROWB + 16;        // padded LDS row stride
   static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row per iteration
   static constexpr int BN = WN * WTN;             // output columns per workgroup
-  static constexpr int LDS_BYTES = 2 * BM * STRIDE;
-  static_assert(WTN % 16 == 0 && BM % 16 == 0 && PF % 2 == 0 && PF >= 2, "tile shape");
+  static constexpr int NW = WN * WK;              // wavefronts per workgroup
+  static constexpr int NA = PF + 1;               // activation stages in LDS
+  static constexpr int STAGE = BM * ROWB;         // bytes per activation stage
+  static_assert(WTN % 16 == 0 && BM % 16 == 0 && PF >= 2 && PF <= 4, "tile shape");
 
   struct Ctx {
     __amdgpu_buffer_rsrc_t act;      // activation rows of the tile (reads past its rows return 0)
     __amdgpu_buffer_rsrc_t w[NMAT];  // this workgroup's weight rows (reads past N return 0)
     int wlane[NSUB];                 // byte offset of this lane's weight row/chunk per subtile
     char* out;                       // output row0
-    char* lds;
+    char* stage[NA];                 // one LDS array per activation stage
     size_t ldo;                      // output row bytes
     int ld;                          // activation/weight row bytes
     int nk, nit, rows, n0, N, wk;
   };
 
+  // LDS swizzle of the activation tile: in row r, the 16-byte chunk c of each
+  // 128-byte K step is stored at chunk c ^ swz(r), so that 16 lanes reading
+  // one chunk of 16 consecutive rows touch 16 distinct 16-byte bank groups.
+  __device__ __forceinline__ static int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+  // s_waitcnt that waits until at most n vector-memory operations of this
+  // wavefront are outstanding (expcnt and lgkmcnt left unconstrained).
+  template <int n>
+  __device__ __forceinline__ static void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  }
+
   template <int MS>
   __device__ __forceinline__ static void run(const Ctx& c) {
-    constexpr int ACH = MS * 16 * CPR;             // activation chunks per iteration
-    constexpr int APT = (ACH + NTH - 1) / NTH;     // chunks per thread
+    // The activation tile of an iteration (MS*16 rows x ROWB bytes) is moved
+    // by LDS-direct buffer loads: one wavefront instruction fills 1 KB of LDS
+    // (lane l writes bytes 16l..16l+15).  NQ instructions per stage, spread
+    // over the wavefronts, QW per wavefront (the last ones repeat the final
+    // instruction so every wavefront issues the same count).
+    constexpr int NQ = MS * 16 * CPR / 64;
+    constexpr int QW = (NQ + NW - 1) / NW;
+    constexpr int WAITN = (PF - 1) * (QW + WL);   // loads issued after iteration it's loads
     const int lane = threadIdx.x & 63;
-    // byte offset of each activation chunk this thread moves (iteration 0);
-    // rows past the tile get an offset past the buffer, which reads as zero
-    int aoff[APT];
+    const int wave = threadIdx.x >> 6;
+    int aoff[QW];
+    int lofs[QW];
 #pragma unroll
-    for (int q = 0; q < APT; ++q) {
-      const int ch = threadIdx.x + q * NTH;
-      const int r = ch / CPR;
-      aoff[q] = (r < c.rows) ? r * c.ld + (ch - r * CPR) * 16 : 0x7ff00000;
+    for (int i = 0; i < QW; ++i) {
+      const int q = min(wave + i * NW, NQ - 1);
+      const int pos = q * 64 + lane;            // 16-byte slot in the stage
+      const int r = pos / CPR;
+      const int pc = pos - r * CPR;
+      const int g = (pc & ~7) | ((pc & 7) ^ swz(r));  // chunk of the row this slot holds
+      aoff[i] = (r < c.rows) ? r * c.ld + g * 16 : 0x7ff00000;
+      lofs[i] = q * 1024;
     }
+    // reader: row jm*16 + lane%16; swz of that row depends on the lane only
+    const int rd = (lane & 15) * ROWB + c.wk * kKB;
+    const int rsw = swz(lane & 15);
 
     f32x4_t acc[NMAT][NSUB][MS];
 #pragma unroll
@@ -113,8 +151,7 @@ struct Gemm {
 #pragma unroll
         for (int jm = 0; jm < MS; ++jm) acc[m][i][jm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 wq[PF][WL];
-    uint4 areg[2][APT];
+    uint4 wq[NA][WL];
 
     auto load_w = [&](int it, uint4* dst) {
       const int s = min(it * WK + c.wk, c.nk - 1);  // clamped: values past the end are unused
@@ -127,33 +164,23 @@ struct Gemm {
             dst[(m * NSUB + i) * 2 + h] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * kKB + h * 64, WAUX));
     };
-    // activation chunks of iteration `it`; past the last iteration the reads
-    // fall past the tile (zero) or onto rows whose values are not used
-    auto load_a = [&](int it, uint4* dst) {
-      const int ko = min(it, c.nit) * ROWB;
+    // activation tile of iteration `it` into LDS stage `st`; past the last
+    // iteration the loads are clamped and their data is never read
+    auto load_a = [&](int it, char* st) {
+      const int itc = min(it, c.nit - 1);
 #pragma unroll
-      for (int q = 0; q < APT; ++q)
-        dst[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(c.act, aoff[q] + ko, 0, 0));
+      for (int i = 0; i < QW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            c.act, (__attribute__((address_space(3))) void*)(st + lofs[i]), 16, aoff[i] + itc * ROWB, 0, 0, 0);
     };
-    auto store_a = [&](int buf, const uint4* src) {
-      char* base = c.lds + buf * (BM * STRIDE);
-#pragma unroll
-      for (int q = 0; q < APT; ++q) {
-        const int ch = threadIdx.x + q * NTH;
-        if (ACH % NTH == 0 || ch < ACH) {
-          const int r = ch / CPR;
-          *reinterpret_cast<uint4*>(base + r * STRIDE + (ch - r * CPR) * 16) = src[q];
-        }
-      }
-    };
-    auto compute = [&](int it, const uint4* w) {
-      const char* lb = c.lds + (it & 1) * (BM * STRIDE) + c.wk * kKB;
+    auto compute = [&](const char* st, const uint4* w) {
+      const char* lb = st + rd;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        const int co = ((h * 4 + (lane >> 4)) ^ rsw) * 16;
         uint4 af[MS];
 #pragma unroll
-        for (int jm = 0; jm < MS; ++jm)
-          af[jm] = *reinterpret_cast<const uint4*>(lb + (jm * 16 + (lane & 15)) * STRIDE + h * 64 + (lane >> 4) * 16);
+        for (int jm = 0; jm < MS; ++jm) af[jm] = *reinterpret_cast<const uint4*>(lb + jm * 16 * ROWB + co);
 #pragma unroll
         for (int jm = 0; jm < MS; ++jm)
 #pragma unroll
@@ -162,35 +189,53 @@ struct Gemm {
             for (int i = 0; i < NSUB; ++i) acc[m][i][jm] = mma16<Tr>(w[(m * NSUB + i) * 2 + h], af[jm], acc[m][i][jm]);
       }
     };
-    auto body = [&](int it, int u) {
-      load_a(it + 2, areg[u & 1]);  // areg[u & 1] held iteration `it`, already in LDS
-      if (WK == 1 || it * WK + c.wk < c.nk) compute(it, wq[u]);
-      load_w(it + PF, wq[u]);
-      store_a((it + 1) & 1, areg[(u + 1) & 1]);
-      __syncthreads();
+    // One iteration `it` (u = it mod NA, so stage and register indices are
+    // compile-time and each LDS stage is its own array: the compiler then
+    // knows loads into one stage do not alias reads of another):
+    //   1. wait until this wavefront's loads of iteration `it` (activation
+    //      tile and weights, issued PF iterations ago) have landed; later
+    //      iterations' loads stay in flight;
+    //   2. barrier (without a release fence, which would drain every
+    //      LDS-direct load): every wavefront's part of the tile is in LDS and
+    //      every wavefront is done with stage (it - 1) mod NA;
+    //   3. issue the activation tile of it + PF into that free stage;
+    //   4. MFMAs of iteration `it`;
+    //   5. issue the weights of it + PF into the registers freed last iteration.
+    auto body = [&](int it, auto uc) {
+      constexpr int u = decltype(uc)::value;
+      wait_vm<WAITN>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      load_a(it + PF, c.stage[(u + PF) % NA]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (WK == 1 || it * WK + c.wk < c.nk) compute(c.stage[u], wq[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(it + PF, wq[(u + PF) % NA]);
     };
 
 #pragma unroll
-    for (int u = 0; u < PF; ++u) load_w(u, wq[u]);
-    load_a(0, areg[0]);
-    load_a(1, areg[1]);
-    store_a(0, areg[0]);
-    __syncthreads();
-
-    int it0 = 0;
-    for (; it0 + PF <= c.nit; it0 += PF) {
-#pragma unroll
-      for (int u = 0; u < PF; ++u) body(it0 + u, u);
+    for (int u = 0; u < PF; ++u) {
+      load_a(u, c.stage[u]);
+      load_w(u, wq[u]);
     }
-#pragma unroll
-    for (int u = 0; u < PF; ++u)
-      if (it0 + u < c.nit) body(it0 + u, u);
+    int it0 = 0;
+    for (; it0 + NA <= c.nit; it0 += NA) {
+      static_for<NA>([&](auto uc) { body(it0 + decltype(uc)::value, uc); });
+    }
+    static_for<NA>([&](auto uc) {
+      if (it0 + decltype(uc)::value < c.nit) body(it0 + decltype(uc)::value, uc);
+    });
+    // the trailing (clamped) loads still write LDS: drain them before the
+    // LDS is reused or the wavefront ends
+    wait_vm<0>();
+    __syncthreads();
 
     if constexpr (WK > 1) {
       // add the partial tiles of wk = 1, 2, ... into wk = 0, in that order
       constexpr int PART = NMAT * NSUB * MS * 4 * 64;  // floats per wavefront partial
-      static_assert((size_t)WN * PART * sizeof(float) <= (size_t)LDS_BYTES, "LDS too small for split-K");
-      float* red = reinterpret_cast<float*>(c.lds) + (size_t)((threadIdx.x >> 6) % WN) * PART;
+      // wavefront column wn reduces through LDS stage wn
+      static_assert((size_t)PART * sizeof(float) <= (size_t)STAGE && WN <= NA, "LDS too small for split-K");
+      float* red = reinterpret_cast<float*>(c.stage[(threadIdx.x >> 6) % WN]);
       for (int src = 1; src < WK; ++src) {
         if (c.wk == src) {
 #pragma unroll
@@ -254,7 +299,12 @@ struct Gemm {
 template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int WAUX>
 __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) {
   using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, WAUX>;
-  __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+  // one LDS array per activation stage (stages past NA are 16-byte stubs)
+  __shared__ __attribute__((aligned(16))) char st0[G::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[G::STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[G::STAGE];
+  __shared__ __attribute__((aligned(16))) char st3[G::NA > 3 ? G::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st4[G::NA > 4 ? G::STAGE : 16];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
@@ -293,7 +343,11 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   const int nbase = nt * G::BN;               // first weight row of the workgroup
   c.n0 = nbase + (wave % WN) * WTN;
   c.out = reinterpret_cast<char*>(p.out) + (size_t)ent.y * c.ldo;
-  c.lds = lds;
+  {
+    char* const all[5] = {st0, st1, st2, st3, st4};
+#pragma unroll
+    for (int i = 0; i < G::NA; ++i) c.stage[i] = all[i];
+  }
   c.act = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(reinterpret_cast<const char*>(p.act) + (size_t)ent.y * ld), (short)0, ent.z * ld, 0x00020000);
   const size_t wbase = (size_t)e * p.N * ld + (size_t)nbase * ld;
