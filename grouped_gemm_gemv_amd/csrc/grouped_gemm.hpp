@@ -103,9 +103,12 @@ struct Gemm {
   };
 
   // LDS swizzle of the activation tile: in row r, the 16-byte chunk c of each
-  // 128-byte K step is stored at chunk c ^ swz(r), so that 16 lanes reading
-  // one chunk of 16 consecutive rows touch 16 distinct 16-byte bank groups.
-  __device__ __forceinline__ static int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+  // 128-byte K step is stored at chunk c ^ (r & 7).  The MFMA operand read
+  // (16-byte lane reads of one chunk of 16 consecutive rows, four chunks per
+  // wavefront) is then free of bank conflicts; measured on gfx950 with the
+  // SQ_LDS_BANK_CONFLICT counter (padding rows by 16 bytes, or other XOR
+  // patterns, gave two-way conflicts).
+  __device__ __forceinline__ static int swz(int r) { return r & 7; }
 
   // s_waitcnt that waits until at most n vector-memory operations of this
   // wavefront are outstanding (expcnt and lgkmcnt left unconstrained).
