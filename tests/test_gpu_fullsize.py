@@ -1,0 +1,104 @@
+"""GPU parity at the workloads' full sizes, through moe_forward (the call the
+benchmark times).
+
+The oracle cannot run whole layers of this size in seconds, so:
+  * routing (when the router runs) is checked for every token against the
+    oracle's float64 logits (ids exact up to near-ties, weights to 2e-6);
+  * every integer dispatch output is checked bit-exactly for every entry;
+  * the layer output is checked on sampled tokens (first, middle, last, and
+    in capacity mode tokens that went through the overflow region) against
+    the oracle's per-token evaluation with the GPU's routing;
+  * capacity mode must give the uncapped output (bitwise with the same tile
+    configuration).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from tests.gpu_helpers import TOL, bits, check_dispatch, check_routing, dev, host64, torch_dtype
+from workloads import WORKLOADS, get_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+FULL = ["mixtral_t512", "mixtral_decode_t1", "mixtral_decode_t8", "mixtral_decode_t32",
+        "mixtral_decode_t128", "mixtral_decode_t256", "mixtral_t4096",
+        "e64_zipf_a0.0", "e64_zipf_a1.2", "e64_zipf_a2.0", "capacity_gini0.10", "capacity_gini0.30"]
+
+
+class WeightCache:
+    """Expert weights on host and device, shared by workloads of one shape."""
+
+    def __init__(self):
+        self.key = None
+
+    def get(self, wl, inp):
+        key = (wl.d, wl.E, wl.F, wl.dtype, wl.w_std)
+        if key != self.key:
+            self.key = None
+            self.host = None
+            self.devw = None
+            torch.cuda.empty_cache()
+            full = make_inputs(wl, 0)
+            self.host = (full.wg, full.wu, full.wd)
+            self.devw = (dev(full.wg), dev(full.wu), dev(full.wd))
+            self.key = key
+        return self.host, self.devw
+
+
+@pytest.fixture(scope="module")
+def weights():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return WeightCache()
+
+
+def _run(wl, inp, devw, capacity=None, tile_rows=0):
+    import grouped_gemm_gemv_amd as M
+    cap = wl.capacity if capacity is None else capacity
+    shape = M.Shape(wl.T, wl.d, wl.E, wl.k, wl.F, cap, torch_dtype(wl.dtype), tile_rows)
+    q = M.query(shape)
+    ws = M.workspace(q.forward_ws_bytes)
+    out = torch.empty((wl.T, wl.d), dtype=torch_dtype(wl.dtype), device="cuda")
+    v = M.moe_forward(shape, dev(inp.x), dev(inp.wr), dev(inp.bias), dev(inp.topk_ids), dev(inp.topk_w),
+                      devw[0], devw[1], devw[2], out, ws)
+    torch.cuda.synchronize()
+    return q, v, out
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fullsize(weights, name):
+    wl = WORKLOADS[name]
+    print(f"\n[gpu fullsize] {name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} F={wl.F} C={wl.capacity}", flush=True)
+    inp = make_inputs(wl, 0, experts=False)
+    host_w, devw = weights.get(wl, inp)
+    q, v, out = _run(wl, inp, devw)
+    ids = v.topk_ids.cpu().numpy()
+    w = v.topk_w.cpu().numpy().astype(np.float64)
+    if inp.topk_ids is None:
+        logits = O.router_logits(inp.x, inp.wr, wl.dtype, inp.bias)
+        differ = check_routing(ids, w, logits, wl.k)
+        assert differ <= max(1, wl.T // 200), differ
+    else:
+        assert np.array_equal(ids, inp.topk_ids)
+    ref_disp = O.dispatch(ids, wl.E, wl.capacity, q.tile_rows)
+    check_dispatch(v.disp.arrays(), ref_disp, wl.E)
+    assert ref_disp["kept_counts"].sum() + ref_disp["spill_counts"].sum() == wl.T * wl.k  # nothing dropped
+    # sampled tokens: ends, middle, and (capacity) tokens with a slot in the overflow region
+    toks = sorted({0, wl.T // 2, wl.T - 1})
+    if wl.capacity:
+        spilled = np.nonzero((ref_disp["row_of"].reshape(wl.T, wl.k) >= wl.E * wl.capacity).any(axis=1))[0]
+        assert spilled.size > 0
+        toks = sorted(set(toks) | set(spilled[[0, spilled.size // 2, -1]].tolist()))
+    ref = O.forward_tokens(inp.x, host_w[0], host_w[1], host_w[2], wl.dtype, ids, w, toks)
+    got = host64(out)[toks]
+    err = float(np.abs(got - ref).max() / np.abs(ref).max())
+    print(f"[gpu fullsize] {name}: sampled tokens {toks} rel err {err:.3e}, tile rows {q.tile_rows}")
+    assert err <= TOL[wl.dtype]
+    if wl.capacity:
+        # the overflow pass gives the uncapped layer output; with the same tile
+        # configuration each (token, expert) row runs the same K loop: bitwise
+        _, _, out0 = _run(wl, inp, devw, capacity=0, tile_rows=q.tile_rows)
+        assert np.array_equal(bits(out), bits(out0))
