@@ -10,6 +10,7 @@ from .api import (
     moe_combine,
     moe_ffn_down,
     moe_ffn_gate_up,
+    moe_ffn_gate_up_gather,
     moe_forward,
     moe_grouped_ffn,
     moe_permute,
@@ -19,6 +20,6 @@ from .api import (
 )
 
 __all__ = [
-    "Dispatch", "ForwardViews", "Shape", "moe_combine", "moe_ffn_down", "moe_ffn_gate_up", "moe_forward",
+    "Dispatch", "ForwardViews", "Shape", "moe_combine", "moe_ffn_down", "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_forward",
     "moe_grouped_ffn", "moe_permute", "moe_route", "query", "workspace",
 ]

@@ -31,7 +31,8 @@ STATUS = {
 
 EXPORTED = [
     "moe_status_string", "moe_query", "moe_dispatch_carve", "moe_route", "moe_permute",
-    "moe_ffn_gate_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine", "moe_forward",
+    "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_grouped_ffn", "moe_combine",
+    "moe_forward",
 ]
 
 
@@ -81,6 +82,7 @@ def _declare(lib):
         "moe_route": [S, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr],
         "moe_permute": [S, c_ptr, c_ptr, D, c_ptr, c_ptr, ctypes.c_size_t, c_ptr],
         "moe_ffn_gate_up": [S, c_ptr, c_ptr, c_ptr, D, ctypes.c_int, c_ptr, c_ptr],
+        "moe_ffn_gate_up_gather": [S, c_ptr, c_ptr, c_ptr, D, ctypes.c_int, c_ptr, c_ptr],
         "moe_ffn_down": [S, c_ptr, c_ptr, D, ctypes.c_int, c_ptr, c_ptr],
         "moe_grouped_ffn": [S, c_ptr, c_ptr, c_ptr, c_ptr, D, c_ptr, c_ptr, c_ptr],
         "moe_combine": [S, c_ptr, c_ptr, D, c_ptr, c_ptr],

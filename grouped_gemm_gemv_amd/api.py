@@ -117,6 +117,12 @@ def moe_ffn_gate_up(shape: Shape, x_perm, w_gate, w_up, disp: Dispatch, pass_idx
                                                    ctypes.byref(disp.c), pass_idx, _p(h), _stream(stream)))
 
 
+def moe_ffn_gate_up_gather(shape: Shape, x, w_gate, w_up, disp: Dispatch, pass_idx: int, h, stream=None):
+    check("moe_ffn_gate_up_gather", lib().moe_ffn_gate_up_gather(
+        ctypes.byref(shape.c()), _p(x), _p(w_gate), _p(w_up), ctypes.byref(disp.c), pass_idx, _p(h),
+        _stream(stream)))
+
+
 def moe_ffn_down(shape: Shape, h, w_down, disp: Dispatch, pass_idx: int, y_perm, stream=None):
     check("moe_ffn_down", lib().moe_ffn_down(ctypes.byref(shape.c()), _p(h), _p(w_down), ctypes.byref(disp.c),
                                              pass_idx, _p(y_perm), _stream(stream)))
@@ -138,7 +144,7 @@ class ForwardViews:
     disp: Dispatch
     topk_ids: torch.Tensor
     topk_w: torch.Tensor
-    x_perm: torch.Tensor
+    x_perm: Optional[torch.Tensor]  # None: moe_forward reads x through token_of
     h: torch.Tensor
     y_perm: torch.Tensor
 
@@ -164,7 +170,7 @@ def moe_forward(shape: Shape, x, w_router, bias, topk_ids, topk_w, w_gate, w_up,
     return ForwardViews(
         disp=Dispatch(shape, c=v.disp, owner=ws),
         topk_ids=ids, topk_w=wts,
-        x_perm=_ws_view(ws, v.x_perm, R * s.d, s.dtype).view(R, s.d),
+        x_perm=None,
         h=_ws_view(ws, v.h, R * s.F, s.dtype).view(R, s.F),
         y_perm=_ws_view(ws, v.y_perm, R * s.d, s.dtype).view(R, s.d),
     )

@@ -97,7 +97,7 @@ struct Plan {
   int nblk;
   DispatchLayout dl;
   size_t permute_ws;      // block counts + block error flags
-  size_t ws_ids, ws_w, ws_disp, ws_perm, ws_xperm, ws_h, ws_y, forward_ws;
+  size_t ws_ids, ws_w, ws_disp, ws_perm, ws_h, ws_y, forward_ws;
 };
 
 Plan make_plan(const moe_shape_t& s) {
@@ -134,7 +134,6 @@ Plan make_plan(const moe_shape_t& s) {
   p.ws_w = take(4 * (size_t)p.Tk);
   p.ws_disp = take(p.dl.bytes);
   p.ws_perm = take(p.permute_ws);
-  p.ws_xperm = take((size_t)p.R * s.d * eb);
   p.ws_h = take((size_t)p.R * s.F * eb);
   p.ws_y = take((size_t)p.R * s.d * eb);
   p.forward_ws = o;
@@ -171,6 +170,7 @@ moe_status_t check_dispatch(const moe_shape_t& s, const Plan& p, const moe_dispa
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Dispatch (count, scan, ranks, tile map) and, if x_perm is not null, the gather.
 moe_status_t enqueue_permute(const moe_shape_t& s, const Plan& p, const void* x, const int32_t* ids,
                              const moe_dispatch_t& d, void* x_perm, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
@@ -198,6 +198,7 @@ moe_status_t enqueue_permute(const moe_shape_t& s, const Plan& p, const void* x,
     a.n_tiles = d.n_tiles;
     a.err_flags = d.err_flags;
     if (moe::launch_dispatch_small(a, st) != hipSuccess) return MOE_ERR_HIP;
+    if (x_perm == nullptr) return MOE_OK;
     return hip_status(moe::launch_gather(x, d.row_of, Tk, s.k, (int64_t)s.d * elt_bytes(s), x_perm, st));
   }
   hipError_t e = moe::launch_count(ids, Tk, s.E, p.nblk, block_counts, block_err, d.token_of, p.R, st);
@@ -222,11 +223,14 @@ moe_status_t enqueue_permute(const moe_shape_t& s, const Plan& p, const void* x,
   if ((e = moe::launch_scatter(ids, Tk, s.k, s.E, s.capacity, p.nblk, block_counts, d.offsets, d.spill_offsets,
                                d.row_of, d.token_of, st)) != hipSuccess)
     return MOE_ERR_HIP;
+  if (x_perm == nullptr) return MOE_OK;
   return hip_status(moe::launch_gather(x, d.row_of, Tk, s.k, (int64_t)s.d * elt_bytes(s), x_perm, st));
 }
 
 moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass, bool gated) {
   moe::GemmArgs a{};
+  a.act_rows = nullptr;
+  a.act_nrows = 0;
   a.tile_off = d.tile_off + pass * (s.E + 1);
   a.tile_map = d.tile_map + (size_t)pass * d.max_tiles * 4;
   a.n_tiles = d.n_tiles + pass;
@@ -237,10 +241,16 @@ moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass,
   return a;
 }
 
+// Gate+up over one pass.  With x_src set, activation row r is read from row
+// token_of[r] of x_src (the gather folded into the GEMM's loads); otherwise
+// from row r of x_perm.
 moe_status_t enqueue_gate_up(const moe_shape_t& s, const void* x_perm, const void* wg, const void* wu,
-                             const moe_dispatch_t& d, int pass, void* h, hipStream_t st) {
+                             const moe_dispatch_t& d, int pass, void* h, hipStream_t st,
+                             const void* x_src = nullptr) {
   moe::GemmArgs a = gemm_args(s, d, pass, true);
-  a.act = x_perm;
+  a.act = x_src != nullptr ? x_src : x_perm;
+  a.act_rows = x_src != nullptr ? d.token_of : nullptr;
+  a.act_nrows = s.T;
   a.w0 = wg;
   a.w1 = wu;
   a.out = h;
@@ -330,6 +340,17 @@ moe_status_t moe_ffn_gate_up(const moe_shape_t* s, const void* x_perm, const voi
   return enqueue_gate_up(*s, x_perm, w_gate, w_up, *disp, pass, h, stream);
 }
 
+moe_status_t moe_ffn_gate_up_gather(const moe_shape_t* s, const void* x, const void* w_gate, const void* w_up,
+                                    const moe_dispatch_t* disp, int pass, void* h, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (!x || !w_gate || !w_up || !h) return MOE_ERR_NULL_PTR;
+  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(*s);
+  if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
+  return enqueue_gate_up(*s, nullptr, w_gate, w_up, *disp, pass, h, stream, x);
+}
+
 moe_status_t moe_ffn_down(const moe_shape_t* s, const void* h, const void* w_down, const moe_dispatch_t* disp,
                           int pass, void* y_perm, hipStream_t stream) {
   moe_status_t st = validate(s);
@@ -382,7 +403,7 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
   char* ws = static_cast<char*>(workspace);
   moe_forward_views_t v{};
   carve(*s, p, ws + p.ws_disp, &v.disp);
-  v.x_perm = ws + p.ws_xperm;
+  v.x_perm = nullptr;  // not materialised: the gate+up GEMM reads x through token_of
   v.h = ws + p.ws_h;
   v.y_perm = ws + p.ws_y;
   if (topk_ids_in != nullptr) {
@@ -398,10 +419,10 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
         hipSuccess)
       return MOE_ERR_HIP;
   }
-  if ((st = enqueue_permute(*s, p, x, v.topk_ids, v.disp, v.x_perm, ws + p.ws_perm, stream)) != MOE_OK) return st;
+  if ((st = enqueue_permute(*s, p, x, v.topk_ids, v.disp, nullptr, ws + p.ws_perm, stream)) != MOE_OK) return st;
   const int passes = s->capacity > 0 ? 2 : 1;
   for (int ps = 0; ps < passes; ++ps) {
-    if ((st = enqueue_gate_up(*s, v.x_perm, w_gate, w_up, v.disp, ps, v.h, stream)) != MOE_OK) return st;
+    if ((st = enqueue_gate_up(*s, nullptr, w_gate, w_up, v.disp, ps, v.h, stream, x)) != MOE_OK) return st;
     if ((st = enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream)) != MOE_OK) return st;
   }
   return hip_status(

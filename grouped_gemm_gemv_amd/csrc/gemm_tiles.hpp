@@ -26,7 +26,7 @@ template <> struct TileCfg<48, true> { using type = TileShape<48, 32, 2, 2, 4>; 
 template <> struct TileCfg<64, true> { using type = TileShape<64, 32, 2, 2, 4>; };
 template <> struct TileCfg<96, true> { using type = TileShape<96, 16, 8, 1, 4>; };
 template <> struct TileCfg<128, true> { using type = TileShape<128, 16, 8, 1, 4>; };
-template <> struct TileCfg<160, true> { using type = TileShape<160, 16, 8, 1, 4>; };
+template <> struct TileCfg<160, true> { using type = TileShape<160, 16, 7, 1, 4>; };
 template <> struct TileCfg<192, true> { using type = TileShape<192, 16, 8, 1, 4>; };
 
 // down projection

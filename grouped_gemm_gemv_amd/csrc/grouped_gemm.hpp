@@ -89,10 +89,11 @@ struct Gemm {
   static constexpr int NW = WN * WK;              // wavefronts per workgroup
   static constexpr int NA = PF + 1;               // activation stages in LDS
   static constexpr int STAGE = BM * ROWB;         // bytes per activation stage
-  static_assert(WTN % 16 == 0 && BM % 16 == 0 && PF >= 2 && PF <= 4, "tile shape");
+  static_assert(WTN % 16 == 0 && BM % 16 == 0 && PF >= 2 && PF <= 7, "tile shape");
 
   struct Ctx {
     __amdgpu_buffer_rsrc_t act;      // activation rows of the tile (reads past its rows return 0)
+    const int32_t* arow;             // null, or source row of each tile row (gather folded into the loads)
     __amdgpu_buffer_rsrc_t w[NMAT];  // this workgroup's weight rows (reads past N return 0)
     int wlane[NSUB];                 // byte offset of this lane's weight row/chunk per subtile
     char* out;                       // output row0
@@ -139,7 +140,8 @@ struct Gemm {
       const int r = pos / CPR;
       const int pc = pos - r * CPR;
       const int g = (pc & ~7) | ((pc & 7) ^ swz(r));  // chunk of the row this slot holds
-      aoff[i] = (r < c.rows) ? r * c.ld + g * 16 : 0x7ff00000;
+      const int src = (r < c.rows) ? (c.arow != nullptr ? c.arow[r] : r) : -1;
+      aoff[i] = (src >= 0) ? src * c.ld + g * 16 : 0x7ff00000;
       lofs[i] = q * 1024;
     }
     // reader: row jm*16 + lane%16; swz of that row depends on the lane only
@@ -308,6 +310,9 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   __shared__ __attribute__((aligned(16))) char st2[G::STAGE];
   __shared__ __attribute__((aligned(16))) char st3[G::NA > 3 ? G::STAGE : 16];
   __shared__ __attribute__((aligned(16))) char st4[G::NA > 4 ? G::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st5[G::NA > 5 ? G::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st6[G::NA > 6 ? G::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st7[G::NA > 7 ? G::STAGE : 16];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
@@ -347,12 +352,19 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   c.n0 = nbase + (wave % WN) * WTN;
   c.out = reinterpret_cast<char*>(p.out) + (size_t)ent.y * c.ldo;
   {
-    char* const all[5] = {st0, st1, st2, st3, st4};
+    char* const all[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
 #pragma unroll
     for (int i = 0; i < G::NA; ++i) c.stage[i] = all[i];
   }
-  c.act = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(reinterpret_cast<const char*>(p.act) + (size_t)ent.y * ld), (short)0, ent.z * ld, 0x00020000);
+  if (p.act_rows != nullptr) {
+    // activation row r of the tile is row act_rows[row0 + r] of the source
+    c.arow = p.act_rows + ent.y;
+    c.act = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.act), (short)0, p.act_nrows * ld, 0x00020000);
+  } else {
+    c.arow = nullptr;
+    c.act = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(p.act) + (size_t)ent.y * ld), (short)0, ent.z * ld, 0x00020000);
+  }
   const size_t wbase = (size_t)e * p.N * ld + (size_t)nbase * ld;
   const int wbytes = min(G::BN, p.N - nbase) * ld;  // reads past N return 0 (column tail)
   c.w[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(reinterpret_cast<const char*>(p.w0) + wbase),

@@ -63,7 +63,9 @@ hipError_t launch_combine(int dtype, const void* y, const float* topk_w, const i
                           int k, int d, void* out, hipStream_t stream);
 
 struct GemmArgs {
-  const void* act;           // [R][K] activation rows
+  const void* act;           // [R][K] activation rows, or (act_rows set) the source rows they come from
+  const int32_t* act_rows;   // null, or [R]: row r of the activations is row act_rows[r] of `act`
+  int act_nrows;             // rows of `act` when act_rows is set
   const void* w0;            // [E][N][K]
   const void* w1;            // [E][N][K] (gate+up: the up projection), else null
   void* out;                 // [R][N]

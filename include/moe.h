@@ -84,8 +84,8 @@ typedef struct moe_sizes {
   int32_t count_blocks;     /* work blocks of the counting step              */
   size_t dispatch_bytes;    /* bytes for moe_dispatch_carve                  */
   size_t permute_ws_bytes;  /* workspace of moe_permute                      */
-  size_t forward_ws_bytes;  /* workspace of moe_forward (includes all of the
-                               above plus x_perm, h, y_perm, ids, weights)   */
+  size_t forward_ws_bytes;  /* workspace of moe_forward (dispatch arrays, the
+                               permute workspace, h, y_perm, ids, weights)   */
 } moe_sizes_t;
 
 /* Dispatch metadata (device arrays), produced by moe_permute and read by the
@@ -159,6 +159,14 @@ moe_status_t moe_ffn_gate_up(const moe_shape_t* s, const void* x_perm, const voi
                              const void* w_up, const moe_dispatch_t* disp, int pass, void* h,
                              hipStream_t stream);
 
+/* moe_ffn_gate_up with the gather folded into the GEMM: activation row r is
+ * read from row disp->token_of[r] of x [T,d] instead of from x_perm.  This
+ * is the kernel moe_forward runs (x_perm is never written); results are
+ * bitwise identical to moe_permute's gather followed by moe_ffn_gate_up. */
+moe_status_t moe_ffn_gate_up_gather(const moe_shape_t* s, const void* x, const void* w_gate,
+                                    const void* w_up, const moe_dispatch_t* disp, int pass, void* h,
+                                    hipStream_t stream);
+
 /* Down-projection grouped GEMM over one pass's tile map (TritonMoE review,
  * desk-editor letter: the down projection is a separate kernel):
  *   y_perm[r, o] = sum_n h[r,n] * w_down[e,o,n]
@@ -186,7 +194,8 @@ typedef struct moe_forward_views {
   moe_dispatch_t disp;  /* dispatch arrays                                     */
   int32_t* topk_ids;    /* [T,k] routing used (computed, or a copy of the input) */
   float* topk_w;        /* [T,k]                                               */
-  void* x_perm;         /* [R,d]                                               */
+  void* x_perm;         /* NULL: moe_forward does not materialise x_perm; its
+                           gate+up GEMM reads row token_of[r] of x directly  */
   void* h;              /* [R,F]                                               */
   void* y_perm;         /* [R,d]                                               */
 } moe_forward_views_t;

@@ -63,7 +63,7 @@ def test_query_sizes_match_definition(name):
         assert q.max_tiles >= O.max_tiles(wl.T, wl.k, wl.E, wl.capacity, q.tile_rows, p)
     assert q.n_passes == (2 if wl.capacity else 1)
     eb = 2 if wl.dtype == "bf16" else 4
-    assert q.forward_ws_bytes >= q.rows * (2 * wl.d + wl.F) * eb + q.dispatch_bytes
+    assert q.forward_ws_bytes >= q.rows * (wl.d + wl.F) * eb + q.dispatch_bytes
 
 
 def test_tile_rows_override():

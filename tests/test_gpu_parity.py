@@ -311,3 +311,17 @@ def test_invalid_ids_flagged_and_skipped():
     M.moe_combine(shape, xp, w, disp, out)
     torch.cuda.synchronize()
     assert np.array_equal(bits(out), bits(x))
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_gate_up_gather_equals_gate_up(runs, case):
+    """The gather folded into the gate+up loads gives h bitwise equal to
+    moe_permute's gather followed by moe_ffn_gate_up."""
+    import grouped_gemm_gemv_amd as M
+    r = runs(case)
+    h2 = torch.zeros_like(r.h)
+    for p in range(r.q.n_passes):
+        M.moe_ffn_gate_up_gather(r.shape, r.x, r.wg, r.wu, r.disp, p, h2)
+    torch.cuda.synchronize()
+    live = r.ref_disp["token_of"] >= 0
+    assert np.array_equal(bits(h2)[live], bits(r.h)[live])
