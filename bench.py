@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first copy 256 MiB device to device 3 times (reference for PMC byte counters)")
     ap.add_argument("--summarize", metavar="DB", help="print a text summary of a rocprofv3 result database and exit")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="print the grouped-GEMM HBM traffic from a FETCH_SIZE and a WRITE_SIZE run "
+                         "(both with --pmc-calibration) and exit")
     return ap.parse_args()
 
 
@@ -99,12 +102,54 @@ def summarize(db_path: str):
         for (name, cn), vals in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
             print(f"{name[:110]} | {cn} | {len(vals)} | {sum(vals) / len(vals):.1f}")
     else:
-        rows = db.execute("select name, count(*), avg(end - start), sum(end - start) from kernels "
-                          "group by name order by sum(end - start) desc").fetchall()
+        acc = collections.defaultdict(list)
+        for name, dur in db.execute("select name, end - start from kernels"):
+            acc[name].append(dur / 1000)
         print(f"# kernel trace summary of {os.path.basename(db_path)}: "
-              "kernel | dispatches | avg us | total us")
-        for name, n, avg, tot in rows:
-            print(f"{name[:110]} | {n} | {avg / 1000:.2f} | {tot / 1000:.1f}")
+              "kernel | dispatches | avg us | median us | total us")
+        for name, d in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+            d = sorted(d)
+            med = d[len(d) // 2] if len(d) % 2 else (d[len(d) // 2 - 1] + d[len(d) // 2]) / 2
+            print(f"{name[:110]} | {len(d)} | {sum(d) / len(d):.2f} | {med:.2f} | {sum(d):.1f}")
+
+
+def pmc_summary(fetch_db: str, write_db: str, workload: str):
+    """HBM bytes per launch of the two grouped GEMMs from rocprofv3 PMC runs.
+
+    Each run starts with three 256 MiB device-to-device copies (--pmc-calibration);
+    their counter readings give the factor from counter KiB to bytes moved."""
+    import sqlite3
+    calib = 256 * 1024 * 1024 / 1024  # KiB copied
+    out = {}
+    for db_path, counter in ((fetch_db, "FETCH_SIZE"), (write_db, "WRITE_SIZE")):
+        db = sqlite3.connect(db_path)
+        rows = db.execute("select name, dispatch_id, counter_value from pmc_events where counter_name = ? "
+                          "order by dispatch_id", (counter,)).fetchall()
+        copies = [v for n, _, v in rows if "copyBuffer" in n][:3]
+        if len(copies) < 3:
+            raise SystemExit(f"{db_path}: fewer than 3 calibration copies")
+        copy_kib = sum(copies) / 3
+        scale = calib / copy_kib
+        out[counter] = (copy_kib, scale)
+        for key, flag in (("gateup", ", true,"), ("down", ", false,")):
+            vals = [v for n, _, v in rows if "grouped_gemm_kernel" in n and flag in n]
+            out[(key, counter)] = (sum(vals) / max(1, len(vals)), len(vals))
+    (cf, sf), (cw, sw) = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    print(f"copy_fetch_kib_per_256MiB: {cf:.1f}  (mean of the 3 calibration copies)")
+    print(f"copy_write_kib_per_256MiB: {cw:.1f}")
+    print(f"fetch_scale: {sf:.4f}")
+    print(f"write_scale: {sw:.4f}")
+    for key in ("gateup", "down"):
+        f, nf = out[(key, "FETCH_SIZE")]
+        w, _ = out[(key, "WRITE_SIZE")]
+        print(f"{key}_fetch_kib_per_launch: {f:.1f}  (dispatches {nf})")
+        print(f"{key}_write_kib_per_launch: {w:.1f}")
+    print(f"workload: {workload}")
+    print(f"gemm_source_sha: {gemm_source_hash()}")
+    for key in ("gateup", "down"):
+        f, _ = out[(key, "FETCH_SIZE")]
+        w, _ = out[(key, "WRITE_SIZE")]
+        print(f"{key}_hbm_bytes_per_launch: {round((f * sf + w * sw) * 1024)}")
 
 
 def gemm_work(wl, counts, dt_bytes):
@@ -147,6 +192,9 @@ def main():
     args = parse()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); "
