@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first copy 256 MiB device to device 3 times (reference for PMC byte counters)")
     ap.add_argument("--summarize", metavar="DB", help="print a text summary of a rocprofv3 result database and exit")
+    ap.add_argument("--cost-curve", action="store_true",
+                    help="per-expert cost curve: time the grouped GEMMs with every expert given n rows, "
+                         "for n from 1 to 1024, fit t = max(a, c + b*n) and exit")
+    ap.add_argument("--cost-experts", type=int, default=8, help="experts per launch for --cost-curve")
+    ap.add_argument("--cost-tile-rows", type=int, default=0, help="tile height for --cost-curve (0: automatic)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print the grouped-GEMM HBM traffic from a FETCH_SIZE and a WRITE_SIZE run "
                          "(both with --pmc-calibration) and exit")
@@ -152,6 +157,107 @@ def pmc_summary(fetch_db: str, write_db: str, workload: str):
         print(f"{key}_hbm_bytes_per_launch: {round((f * sf + w * sw) * 1024)}")
 
 
+def fit_knee(n, t):
+    """Least-squares fit of t = max(a, c + b*n): flat up to a knee, then linear.
+    Returns (a, c, b, n_star) with n_star = (a - c) / b, the knee."""
+    n = np.asarray(n, dtype=np.float64)
+    t = np.asarray(t, dtype=np.float64)
+    best = None
+    for i in range(1, len(n) - 1):
+        a = float(np.mean(t[:i]))
+        b, c = np.polyfit(n[i:], t[i:], 1)
+        if b <= 0:
+            continue
+        sse = float(np.sum((np.maximum(a, c + b * n) - t) ** 2))
+        if best is None or sse < best[0]:
+            best = (sse, a, float(c), float(b))
+    if best is None:
+        return None
+    _, a, c, b = best
+    return a, c, b, (a - c) / b
+
+
+def cost_curve(args):
+    """Time one pass of the two grouped GEMMs when each of `--cost-experts`
+    experts holds exactly n rows, for n = 1 ... 1024, at the workload's d and F.
+
+    The cost of an expert's GEMMs is flat in n while its weight stream bounds
+    it and grows linearly once the matrix cores do (the TEMPO review, per-expert
+    cost model); the fitted knee n* is where the layer leaves the
+    weight-streaming regime on this GPU."""
+    import torch
+
+    import grouped_gemm_gemv_amd as M
+    from workloads import get_workload
+
+    wl = get_workload(args.workload)
+    Eg = args.cost_experts
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dt_bytes = 2 if wl.dtype == "bf16" else 4
+    peak_f = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    g = torch.Generator(device="cuda").manual_seed(args.seed)
+    wg = (torch.randn((Eg, wl.F, wl.d), device="cuda", generator=g) * 0.02).to(dt)
+    wu = (torch.randn((Eg, wl.F, wl.d), device="cuda", generator=g) * 0.02).to(dt)
+    wd = (torch.randn((Eg, wl.d, wl.F), device="cuda", generator=g) * 0.02).to(dt)
+    cur = torch.cuda.current_stream()
+    rows = [1, 2, 4, 8, 16, 24, 32, 48, 64, 80, 96, 128, 160, 192, 224, 256, 320, 384, 448, 512, 640, 768, 1024]
+    res = []
+    print(f"# per-expert cost curve: {Eg} experts x n rows, d={wl.d}, F={wl.F}, {wl.dtype}; "
+          f"one gate+up and one down launch, HIP events, median of 5 runs of {args.kernel_iters} calls")
+    print("# n | tile rows | gate+up us | down us | total us | us per expert | TFLOP/s | weight TB/s")
+    for n in rows:
+        T = n * Eg
+        shape = M.Shape(T, wl.d, Eg, 1, wl.F, 0, dt, args.cost_tile_rows)
+        q = M.query(shape)
+        x = (torch.randn((T, wl.d), device="cuda", generator=g)).to(dt)
+        ids = (torch.arange(T, device="cuda", dtype=torch.int32) // n).reshape(T, 1).contiguous()
+        w = torch.ones((T, 1), device="cuda", dtype=torch.float32)
+        ws = M.workspace(q.forward_ws_bytes)
+        out = torch.empty((T, wl.d), dtype=dt, device="cuda")
+        v = M.moe_forward(shape, x, None, None, ids, w, wg, wu, wd, out, ws)
+        torch.cuda.synchronize()
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            meas = []
+            for _ in range(5):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(cur)
+                for _ in range(args.kernel_iters):
+                    fn()
+                b.record(cur)
+                b.synchronize()
+                meas.append(a.elapsed_time(b) / args.kernel_iters * 1e3)
+            return float(np.median(meas))
+
+        t_gu = timed(lambda: M.moe_ffn_gate_up_gather(shape, x, wg, wu, v.disp, 0, v.h))
+        t_dn = timed(lambda: M.moe_ffn_down(shape, v.h, wd, v.disp, 0, v.y_perm))
+        tot = t_gu + t_dn
+        flops = 2.0 * T * 3 * wl.d * wl.F
+        wbytes = 3.0 * Eg * wl.d * wl.F * dt_bytes
+        res.append((n, q.tile_rows, t_gu, t_dn, tot))
+        print(f"{n} | {q.tile_rows} | {t_gu:.1f} | {t_dn:.1f} | {tot:.1f} | {tot / Eg:.2f} | "
+              f"{flops / tot / 1e6:.1f} | {wbytes / tot / 1e6:.2f}", flush=True)
+        del x, ids, w, ws, out, v
+    n_arr = [r[0] for r in res]
+    fit = fit_knee(n_arr, [r[4] for r in res])
+    hbm_eff = 3.0 * Eg * wl.d * wl.F * dt_bytes / (res[0][4] * 1e-6) / (PEAK_HBM_GBS * 1e9)
+    mfma_eff = 2.0 * res[-1][0] * Eg * 3 * wl.d * wl.F / (res[-1][4] * 1e-6) / (peak_f * 1e12)
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9) * (dt_bytes / 2)
+    summary = {"experts": Eg, "d": wl.d, "F": wl.F, "dtype": wl.dtype,
+               "hbm_eff_at_n1": round(hbm_eff, 4), "mfma_eff_at_nmax": round(mfma_eff, 4),
+               "ridge_rows_datasheet": round(ridge, 1),
+               "ridge_rows_measured_eff": round(ridge * mfma_eff / hbm_eff, 1)}
+    if fit is not None:
+        a, c, b, nstar = fit
+        summary.update({"fit_flat_us": round(a, 2), "fit_intercept_us": round(c, 2),
+                        "fit_us_per_row": round(b, 4), "n_star": round(nstar, 1)})
+    print("# fit of total us = max(a, c + b*n) and ridge estimates:")
+    print(json.dumps(summary), flush=True)
+
+
 def gemm_work(wl, counts, dt_bytes):
     """Algorithmic FLOPs and HBM bytes of the two grouped GEMMs (per launch)."""
     Tk = wl.T * wl.k
@@ -195,6 +301,12 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
+    if args.cost_curve:
+        if args.gpus != 1:
+            print("the cost curve runs on one GPU", file=sys.stderr)
+            sys.exit(2)
+        cost_curve(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); "

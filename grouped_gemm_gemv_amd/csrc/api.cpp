@@ -18,11 +18,19 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest row-tile height of the grouped GEMMs.  A tile holds up to BM rows
-// and only its non-empty 16-row subtiles are computed, so BM is chosen to
-// cover an active expert's rows with one tile (1.25x the mean of T*k spread
-// over min(E, T*k) experts, at most C in the capacity pass): each expert's
-// weights then stream from HBM once.
+// and only its non-empty 16-row subtiles are computed, so a tall tile costs
+// nothing for short experts.  The tall configurations (BM 160/192: 112- or
+// 128-column workgroups, K not split) stream weights best and give a hot
+// expert the fewest row tiles, but need enough column tiles to occupy every
+// compute unit: they are used when the down projection alone has at least
+// one 128-column tile per compute unit over the experts that can be active.
+// BM 160 is the 112-column gate+up tile, used when 112 divides F and the
+// mean expert fits in it.  Otherwise (few active experts, decode) the tile
+// covers an active expert's rows with one tile (1.25x the mean of T*k over
+// min(E, T*k) experts, at most C in the capacity pass), and the short
+// configurations split K across wavefronts so that there are enough units.
 constexpr int kTileRows[] = {16, 32, 48, 64, 96, 128, 160, 192};
+constexpr int kComputeUnits = 256;
 
 bool supported_tile_rows(int bm) {
   for (int v : kTileRows)
@@ -33,8 +41,10 @@ bool supported_tile_rows(int bm) {
 int choose_tile_rows(const moe_shape_t& s) {
   if (s.tile_rows != 0) return s.tile_rows;
   const int64_t Tk = (int64_t)s.T * s.k;
-  int64_t mean = ceil_div(Tk, std::min<int64_t>(s.E, Tk));
+  const int64_t active = std::min<int64_t>(s.E, Tk);
+  int64_t mean = ceil_div(Tk, active);
   if (s.capacity > 0) mean = std::min<int64_t>(mean, s.capacity);
+  if (active * ceil_div(s.d, 128) >= kComputeUnits) return (mean <= 160 && s.F % 112 == 0) ? 160 : 192;
   const int64_t want = std::max<int64_t>(mean, (mean * 5 + 3) / 4);
   for (int v : kTileRows)
     if (v >= want) return v;
@@ -238,6 +248,7 @@ moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass,
   a.K = gated ? s.d : s.F;
   a.N = gated ? s.F : s.d;
   a.max_tiles = (int)pass_max_tiles(s, d.tile_rows, pass);
+  a.xcd_chunk = 8;
   return a;
 }
 

@@ -50,7 +50,13 @@
 // (J = units per XCD).  Each XCD therefore walks a contiguous range of units,
 // ordered expert-major, then column tile, then row tile: the row tiles that
 // share one weight column tile run back to back on one XCD and share its L2,
-// and the activation rows of one expert stay in that XCD's L2.
+// and the activation rows of one expert stay in that XCD's L2.  When the
+// routing is skewed (a few experts hold several row tiles each), contiguous
+// ranges would put a hot expert's compute-heavy units on one or two XCDs;
+// the units are then dealt to the XCDs in chunks of S consecutive units
+// (chunk c to XCD c mod 8), which spreads every expert over the chip while
+// consecutive units still share an XCD.  The test uses only the tile counts
+// per expert, read on the device, so every workgroup takes the same mapping.
 #pragma once
 
 #include <type_traits>
@@ -318,11 +324,33 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
 
   // ---- which (expert, row tile, column tile) this workgroup computes
   const int NT = (p.N + G::BN - 1) / G::BN;
-  const int total = p.n_tiles[0] * NT;
-  const int J = (total + 7) >> 3;
+  const int ntiles = p.n_tiles[0];
+  const int total = ntiles * NT;
   const int j = blockIdx.x >> 3;
-  if (j >= J) return;
-  const int L = (blockIdx.x & 7) * J + j;
+  // Skew test, identical in every workgroup: are some experts' tile counts
+  // well above the mean over active experts (max * active > 2 * tiles)?
+  bool skewed = false;
+  if (p.xcd_chunk > 0) {
+    int mx = 0, act = 0;
+    for (int b = 0; b < p.E; b += 64) {
+      const int i = b + lane;
+      const int t = (i < p.E) ? p.tile_off[i + 1] - p.tile_off[i] : 0;
+      mx = max(mx, t);
+      act += __popcll(__ballot(t > 0));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+    skewed = (long long)mx * act > 2LL * ntiles;
+  }
+  int L;
+  if (!skewed) {
+    const int J = (total + 7) >> 3;
+    if (j >= J) return;
+    L = (blockIdx.x & 7) * J + j;
+  } else {
+    const int q = j / p.xcd_chunk;
+    L = ((q << 3) + (blockIdx.x & 7)) * p.xcd_chunk + (j - q * p.xcd_chunk);
+  }
   if (L >= total) return;
   // expert e owns units [tile_off[e] * NT, tile_off[e+1] * NT)
   int e = 0;
@@ -383,7 +411,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   constexpr int BN = Cfg::WN * Cfg::WTN;
   const int NT = (a.N + BN - 1) / BN;
   const long long units = (long long)a.max_tiles * NT;
-  const long long grid = ((units + 7) / 8) * 8;
+  const long long round = a.xcd_chunk > 0 ? 8LL * a.xcd_chunk : 8;  // chunked mapping: whole rounds of chunks
+  const long long grid = ((units + round - 1) / round) * round;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::WAUX>),
                      dim3((unsigned)grid), dim3(64 * Cfg::WN * Cfg::WK), 0, stream, a);

@@ -74,6 +74,7 @@ struct GemmArgs {
   const int32_t* n_tiles;    // [1] of this pass
   int E, K, N;
   int max_tiles;
+  int xcd_chunk;             // S > 0: uneven tile counts per expert deal chunks of S units to the XCDs in turn
 };
 
 hipError_t launch_gemm_bf16_gateup(int BM, const GemmArgs& a, hipStream_t stream);

@@ -12,7 +12,7 @@ import pytest
 from grouped_gemm_gemv_amd import _lib
 from grouped_gemm_gemv_amd._lib import MoeDispatch, MoeForwardViews, MoeShape, MoeSizes
 from oracle import moe_oracle as O
-from workloads import WORKLOADS
+from workloads import WORKLOADS, get_workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
@@ -72,6 +72,22 @@ def test_tile_rows_override():
         assert st == 0 and q.tile_rows == bm
         for p in (0, 1):
             assert q.max_tiles >= O.max_tiles(300, 4, 16, 40, bm, p)
+
+
+@pytest.mark.parametrize("name,bm", [
+    ("mixtral_t512", 160),        # 8 experts x 32 down column tiles fill the 256 compute units; 112 | F
+    ("mixtral_t4096", 192),       # mean 1024 rows: the tallest tile
+    ("mixtral_decode_t1", 16),    # 2 active experts: split-K short tiles keep the units up
+    ("mixtral_decode_t8", 160),   # min(E, T*k) = 8 experts can be active
+    ("mixtral_decode_t128", 160),
+    ("e64_zipf_a2.0", 192),       # 112 does not divide F = 2560
+    ("capacity_gini0.10", 192),
+    ("tiny_f32", 32),             # one 128-column down tile per expert: mean 16 -> 1.25x -> 32
+])
+def test_automatic_tile_rows(name, bm):
+    wl = get_workload(name)
+    st, q = _query(_shape(T=wl.T, d=wl.d, E=wl.E, k=wl.k, F=wl.F, C=wl.capacity))
+    assert st == 0 and q.tile_rows == bm
 
 
 def test_capacity_rows_example():
