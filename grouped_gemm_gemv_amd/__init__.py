@@ -9,6 +9,9 @@ from .api import (
     Shape,
     moe_combine,
     moe_ffn_down,
+    moe_ffn_down_fp8,
+    moe_ffn_gate_up_fp8,
+    moe_forward_fp8,
     moe_ffn_gate_up,
     moe_ffn_gate_up_gather,
     moe_forward,
@@ -21,5 +24,6 @@ from .api import (
 
 __all__ = [
     "Dispatch", "ForwardViews", "Shape", "moe_combine", "moe_ffn_down", "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_forward",
+    "moe_ffn_gate_up_fp8", "moe_ffn_down_fp8", "moe_forward_fp8",
     "moe_grouped_ffn", "moe_permute", "moe_route", "query", "workspace",
 ]

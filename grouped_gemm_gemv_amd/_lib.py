@@ -32,7 +32,7 @@ STATUS = {
 EXPORTED = [
     "moe_status_string", "moe_query", "moe_dispatch_carve", "moe_route", "moe_permute",
     "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_grouped_ffn", "moe_combine",
-    "moe_forward",
+    "moe_forward", "moe_ffn_gate_up_fp8", "moe_ffn_down_fp8", "moe_forward_fp8",
 ]
 
 
@@ -88,6 +88,10 @@ def _declare(lib):
         "moe_combine": [S, c_ptr, c_ptr, D, c_ptr, c_ptr],
         "moe_forward": [S, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                         ctypes.c_size_t, P(MoeForwardViews), c_ptr],
+        "moe_ffn_gate_up_fp8": [S, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, D, ctypes.c_int, c_ptr, c_ptr],
+        "moe_ffn_down_fp8": [S, c_ptr, c_ptr, c_ptr, D, ctypes.c_int, c_ptr, c_ptr],
+        "moe_forward_fp8": [S, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
+                            c_ptr, c_ptr, ctypes.c_size_t, P(MoeForwardViews), c_ptr],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -123,6 +123,21 @@ def moe_ffn_gate_up_gather(shape: Shape, x, w_gate, w_up, disp: Dispatch, pass_i
         _stream(stream)))
 
 
+def moe_ffn_gate_up_fp8(shape: Shape, x, w_gate, w_up, s_gate, s_up, disp: Dispatch, pass_idx: int, h,
+                        stream=None):
+    """Gate+up with E4M3 weight codes (uint8 [E,F,d]) and per-channel fp32 scales [E,F]."""
+    check("moe_ffn_gate_up_fp8", lib().moe_ffn_gate_up_fp8(
+        ctypes.byref(shape.c()), _p(x), _p(w_gate), _p(w_up), _p(s_gate), _p(s_up), ctypes.byref(disp.c),
+        pass_idx, _p(h), _stream(stream)))
+
+
+def moe_ffn_down_fp8(shape: Shape, h, w_down, s_down, disp: Dispatch, pass_idx: int, y_perm, stream=None):
+    """Down projection with E4M3 weight codes (uint8 [E,d,F]) and per-channel fp32 scales [E,d]."""
+    check("moe_ffn_down_fp8", lib().moe_ffn_down_fp8(ctypes.byref(shape.c()), _p(h), _p(w_down), _p(s_down),
+                                                     ctypes.byref(disp.c), pass_idx, _p(y_perm),
+                                                     _stream(stream)))
+
+
 def moe_ffn_down(shape: Shape, h, w_down, disp: Dispatch, pass_idx: int, y_perm, stream=None):
     check("moe_ffn_down", lib().moe_ffn_down(ctypes.byref(shape.c()), _p(h), _p(w_down), ctypes.byref(disp.c),
                                              pass_idx, _p(y_perm), _stream(stream)))
@@ -155,13 +170,7 @@ def _ws_view(ws: torch.Tensor, ptr: int, n: int, dtype) -> torch.Tensor:
     return ws[off:off + n * esz].view(dtype)
 
 
-def moe_forward(shape: Shape, x, w_router, bias, topk_ids, topk_w, w_gate, w_up, w_down, out, ws,
-                stream=None) -> ForwardViews:
-    """The whole layer; returns views of the intermediates inside `ws`."""
-    v = MoeForwardViews()
-    check("moe_forward", lib().moe_forward(ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(topk_ids),
-                                           _p(topk_w), _p(w_gate), _p(w_up), _p(w_down), _p(out), _p(ws),
-                                           ws.numel(), ctypes.byref(v), _stream(stream)))
+def _forward_views(shape: Shape, v, ws, topk_ids, topk_w) -> ForwardViews:
     R = query(shape).rows
     Tk = shape.T * shape.k
     s = shape
@@ -174,3 +183,24 @@ def moe_forward(shape: Shape, x, w_router, bias, topk_ids, topk_w, w_gate, w_up,
         h=_ws_view(ws, v.h, R * s.F, s.dtype).view(R, s.F),
         y_perm=_ws_view(ws, v.y_perm, R * s.d, s.dtype).view(R, s.d),
     )
+
+
+def moe_forward(shape: Shape, x, w_router, bias, topk_ids, topk_w, w_gate, w_up, w_down, out, ws,
+                stream=None) -> ForwardViews:
+    """The whole layer; returns views of the intermediates inside `ws`."""
+    v = MoeForwardViews()
+    check("moe_forward", lib().moe_forward(ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(topk_ids),
+                                           _p(topk_w), _p(w_gate), _p(w_up), _p(w_down), _p(out), _p(ws),
+                                           ws.numel(), ctypes.byref(v), _stream(stream)))
+    return _forward_views(shape, v, ws, topk_ids, topk_w)
+
+
+def moe_forward_fp8(shape: Shape, x, w_router, bias, topk_ids, topk_w, w_gate, w_up, w_down, s_gate, s_up,
+                    s_down, out, ws, stream=None) -> ForwardViews:
+    """The whole layer with E4M3 expert weight codes and per-channel fp32 scales."""
+    v = MoeForwardViews()
+    check("moe_forward_fp8", lib().moe_forward_fp8(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(topk_ids), _p(topk_w), _p(w_gate), _p(w_up),
+        _p(w_down), _p(s_gate), _p(s_up), _p(s_down), _p(out), _p(ws), ws.numel(), ctypes.byref(v),
+        _stream(stream)))
+    return _forward_views(shape, v, ws, topk_ids, topk_w)

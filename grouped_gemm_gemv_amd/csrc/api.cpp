@@ -248,7 +248,7 @@ moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass,
   a.K = gated ? s.d : s.F;
   a.N = gated ? s.F : s.d;
   a.max_tiles = (int)pass_max_tiles(s, d.tile_rows, pass);
-  a.xcd_chunk = 8;
+  a.skew_map = 1;
   return a;
 }
 
@@ -257,8 +257,10 @@ moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass,
 // from row r of x_perm.
 moe_status_t enqueue_gate_up(const moe_shape_t& s, const void* x_perm, const void* wg, const void* wu,
                              const moe_dispatch_t& d, int pass, void* h, hipStream_t st,
-                             const void* x_src = nullptr) {
+                             const void* x_src = nullptr, const float* sg = nullptr, const float* su = nullptr) {
   moe::GemmArgs a = gemm_args(s, d, pass, true);
+  a.s0 = sg;
+  a.s1 = su;
   a.act = x_src != nullptr ? x_src : x_perm;
   a.act_rows = x_src != nullptr ? d.token_of : nullptr;
   a.act_nrows = s.T;
@@ -269,13 +271,57 @@ moe_status_t enqueue_gate_up(const moe_shape_t& s, const void* x_perm, const voi
 }
 
 moe_status_t enqueue_down(const moe_shape_t& s, const void* h, const void* wd, const moe_dispatch_t& d, int pass,
-                          void* y, hipStream_t st) {
+                          void* y, hipStream_t st, const float* sd = nullptr) {
   moe::GemmArgs a = gemm_args(s, d, pass, false);
+  a.s0 = sd;
   a.act = h;
   a.w0 = wd;
   a.w1 = nullptr;
   a.out = y;
   return hip_status(moe::launch_grouped_gemm(s.dtype, false, d.tile_rows, a, st));
+}
+
+// The whole layer; s_gate/s_up/s_down non-null: the weights are E4M3 codes.
+moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
+                          const int32_t* topk_ids_in, const float* topk_w_in, const void* w_gate, const void* w_up,
+                          const void* w_down, const float* s_gate, const float* s_up, const float* s_down, void* out,
+                          void* workspace, size_t ws_bytes, moe_forward_views_t* views_out, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (!x || !w_gate || !w_up || !w_down || !out || !workspace) return MOE_ERR_NULL_PTR;
+  if ((topk_ids_in == nullptr) != (topk_w_in == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (topk_ids_in == nullptr && w_router == nullptr) return MOE_ERR_NULL_PTR;
+  const Plan p = make_plan(*s);
+  if (ws_bytes < p.forward_ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return MOE_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  moe_forward_views_t v{};
+  carve(*s, p, ws + p.ws_disp, &v.disp);
+  v.x_perm = nullptr;  // not materialised: the gate+up GEMM reads x through token_of
+  v.h = ws + p.ws_h;
+  v.y_perm = ws + p.ws_y;
+  if (topk_ids_in != nullptr) {
+    v.topk_ids = const_cast<int32_t*>(topk_ids_in);
+    v.topk_w = const_cast<float*>(topk_w_in);
+  } else {
+    v.topk_ids = reinterpret_cast<int32_t*>(ws + p.ws_ids);
+    v.topk_w = reinterpret_cast<float*>(ws + p.ws_w);
+  }
+  if (views_out != nullptr) *views_out = v;
+  if (topk_ids_in == nullptr) {
+    if (moe::launch_route(s->dtype, x, w_router, bias, s->T, s->d, s->E, s->k, v.topk_ids, v.topk_w, stream) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if ((st = enqueue_permute(*s, p, x, v.topk_ids, v.disp, nullptr, ws + p.ws_perm, stream)) != MOE_OK) return st;
+  const int passes = s->capacity > 0 ? 2 : 1;
+  for (int ps = 0; ps < passes; ++ps) {
+    if ((st = enqueue_gate_up(*s, nullptr, w_gate, w_up, v.disp, ps, v.h, stream, x, s_gate, s_up)) != MOE_OK)
+      return st;
+    if ((st = enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream, s_down)) != MOE_OK) return st;
+  }
+  return hip_status(
+      moe::launch_combine(s->dtype, v.y_perm, v.topk_w, v.disp.row_of, s->T, s->k, s->d, out, stream));
 }
 
 }  // namespace
@@ -403,41 +449,46 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
                          const int32_t* topk_ids_in, const float* topk_w_in, const void* w_gate, const void* w_up,
                          const void* w_down, void* out, void* workspace, size_t ws_bytes,
                          moe_forward_views_t* views_out, hipStream_t stream) {
+  return forward_impl(s, x, w_router, bias, topk_ids_in, topk_w_in, w_gate, w_up, w_down, nullptr, nullptr,
+                      nullptr, out, workspace, ws_bytes, views_out, stream);
+}
+
+moe_status_t moe_ffn_gate_up_fp8(const moe_shape_t* s, const void* x, const uint8_t* w_gate, const uint8_t* w_up,
+                                 const float* s_gate, const float* s_up, const moe_dispatch_t* disp, int pass,
+                                 void* h, hipStream_t stream) {
   moe_status_t st = validate(s);
   if (st != MOE_OK) return st;
-  if (!x || !w_gate || !w_up || !w_down || !out || !workspace) return MOE_ERR_NULL_PTR;
-  if ((topk_ids_in == nullptr) != (topk_w_in == nullptr)) return MOE_ERR_INVALID_ARG;
-  if (topk_ids_in == nullptr && w_router == nullptr) return MOE_ERR_NULL_PTR;
+  if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!x || !w_gate || !w_up || !s_gate || !s_up || !h) return MOE_ERR_NULL_PTR;
+  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(*s);
-  if (ws_bytes < p.forward_ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return MOE_ERR_INVALID_ARG;
-  char* ws = static_cast<char*>(workspace);
-  moe_forward_views_t v{};
-  carve(*s, p, ws + p.ws_disp, &v.disp);
-  v.x_perm = nullptr;  // not materialised: the gate+up GEMM reads x through token_of
-  v.h = ws + p.ws_h;
-  v.y_perm = ws + p.ws_y;
-  if (topk_ids_in != nullptr) {
-    v.topk_ids = const_cast<int32_t*>(topk_ids_in);
-    v.topk_w = const_cast<float*>(topk_w_in);
-  } else {
-    v.topk_ids = reinterpret_cast<int32_t*>(ws + p.ws_ids);
-    v.topk_w = reinterpret_cast<float*>(ws + p.ws_w);
-  }
-  if (views_out != nullptr) *views_out = v;
-  if (topk_ids_in == nullptr) {
-    if (moe::launch_route(s->dtype, x, w_router, bias, s->T, s->d, s->E, s->k, v.topk_ids, v.topk_w, stream) !=
-        hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  if ((st = enqueue_permute(*s, p, x, v.topk_ids, v.disp, nullptr, ws + p.ws_perm, stream)) != MOE_OK) return st;
-  const int passes = s->capacity > 0 ? 2 : 1;
-  for (int ps = 0; ps < passes; ++ps) {
-    if ((st = enqueue_gate_up(*s, nullptr, w_gate, w_up, v.disp, ps, v.h, stream, x)) != MOE_OK) return st;
-    if ((st = enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream)) != MOE_OK) return st;
-  }
-  return hip_status(
-      moe::launch_combine(s->dtype, v.y_perm, v.topk_w, v.disp.row_of, s->T, s->k, s->d, out, stream));
+  if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
+  return enqueue_gate_up(*s, nullptr, w_gate, w_up, *disp, pass, h, stream, x, s_gate, s_up);
+}
+
+moe_status_t moe_ffn_down_fp8(const moe_shape_t* s, const void* h, const uint8_t* w_down, const float* s_down,
+                              const moe_dispatch_t* disp, int pass, void* y_perm, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!h || !w_down || !s_down || !y_perm) return MOE_ERR_NULL_PTR;
+  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(*s);
+  if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
+  return enqueue_down(*s, h, w_down, *disp, pass, y_perm, stream, s_down);
+}
+
+moe_status_t moe_forward_fp8(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
+                             const int32_t* topk_ids_in, const float* topk_w_in, const uint8_t* w_gate,
+                             const uint8_t* w_up, const uint8_t* w_down, const float* s_gate, const float* s_up,
+                             const float* s_down, void* out, void* workspace, size_t ws_bytes,
+                             moe_forward_views_t* views_out, hipStream_t stream) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!s_gate || !s_up || !s_down) return MOE_ERR_NULL_PTR;
+  return forward_impl(s, x, w_router, bias, topk_ids_in, topk_w_in, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                      out, workspace, ws_bytes, views_out, stream);
 }
 
 }  // extern "C"

@@ -53,7 +53,7 @@
 // and the activation rows of one expert stay in that XCD's L2.  When the
 // routing is skewed (a few experts hold several row tiles each), contiguous
 // ranges would put a hot expert's compute-heavy units on one or two XCDs;
-// the units are then dealt to the XCDs in chunks of S consecutive units
+// the units are then dealt to the XCDs in chunks of 8 consecutive units
 // (chunk c to XCD c mod 8), which spreads every expert over the chip while
 // consecutive units still share an XCD.  The test uses only the tile counts
 // per expert, read on the device, so every workgroup takes the same mapping.
@@ -68,7 +68,8 @@
 namespace moe {
 namespace gemm {
 
-constexpr int kKB = 128;  // bytes of K per step
+constexpr int kKB = 128;      // bytes of K per step
+constexpr int kXcdChunk = 8;  // units per chunk of the skewed workgroup-to-XCD mapping
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time unroll).
 template <int N, int I = 0, class F>
@@ -81,14 +82,29 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int WAUX>
+// Eight OCP E4M3 codes (two dwords, code j of the pair in byte j) widened to
+// the eight bf16 values of one MFMA operand.  Every E4M3 value is exactly a
+// bf16 value, so the widening is exact (scale 1; the channel scale is applied
+// to the fp32 result).
+__device__ __forceinline__ uint4 widen_e4m3(unsigned lo, unsigned hi) {
+  return uint4{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+
+// WQ: the weights are OCP E4M3 codes with one fp32 scale per output channel
+// (weight row); the activations stay bf16.
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int WAUX, bool WQ>
 struct Gemm {
   using Elt = typename Tr::T;
+  static_assert(!WQ || std::is_same<Tr, TBF16>::value, "fp8 weights take bf16 activations");
   static constexpr int NTH = 64 * WN * WK;
   static constexpr int NSUB = WTN / 16;
   static constexpr int NMAT = GATED ? 2 : 1;
   static constexpr int MSUB = BM / 16;
-  static constexpr int WL = NMAT * NSUB * 2;      // 16-byte weight loads per lane per step
+  static constexpr int WL = NMAT * NSUB * (WQ ? 1 : 2);  // 16-byte weight loads per lane per step
+  static constexpr int KWB = WQ ? kKB / 2 : kKB;  // weight bytes per row per step (64 K elements)
   static constexpr int ROWB = WK * kKB;           // activation bytes per row per iteration
   static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row per iteration
   static constexpr int BN = WN * WTN;             // output columns per workgroup
@@ -102,6 +118,7 @@ struct Gemm {
     const int32_t* arow;             // null, or source row of each tile row (gather folded into the loads)
     __amdgpu_buffer_rsrc_t w[NMAT];  // this workgroup's weight rows (reads past N return 0)
     int wlane[NSUB];                 // byte offset of this lane's weight row/chunk per subtile
+    const float* scale[NMAT];        // fp8 weights: per-channel scales of this expert
     char* out;                       // output row0
     char* stage[NA];                 // one LDS array per activation stage
     size_t ldo;                      // output row bytes
@@ -166,14 +183,24 @@ struct Gemm {
 
     auto load_w = [&](int it, uint4* dst) {
       const int s = min(it * WK + c.wk, c.nk - 1);  // clamped: values past the end are unused
+      if constexpr (WQ) {
+        // one 16-byte load holds this lane's codes of both K halves
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int i = 0; i < NSUB; ++i)
+          for (int i = 0; i < NSUB; ++i)
+            dst[m * NSUB + i] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * KWB, WAUX));
+      } else {
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-            dst[(m * NSUB + i) * 2 + h] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * kKB + h * 64, WAUX));
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              dst[(m * NSUB + i) * 2 + h] = __builtin_bit_cast(
+                  uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * kKB + h * 64, WAUX));
+      }
     };
     // activation tile of iteration `it` into LDS stage `st`; past the last
     // iteration the loads are clamped and their data is never read
@@ -184,20 +211,34 @@ struct Gemm {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             c.act, (__attribute__((address_space(3))) void*)(st + lofs[i]), 16, aoff[i] + itc * ROWB, 0, 0, 0);
     };
+    // MFMA operands of one step, half h (32 of its 64 K elements).  bf16
+    // weights: lane group g = lane/16 holds elements 32h + 8g .. +7 of both
+    // operands.  fp8 weights: a lane's 16 codes are elements 16g .. 16g+15,
+    // so half h takes elements 16g + 8h .. +7, and the activation read follows
+    // the same order (any K order shared by both operands gives the same sum).
     auto compute = [&](const char* st, const uint4* w) {
       const char* lb = st + rd;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int co = ((h * 4 + (lane >> 4)) ^ rsw) * 16;
+        const int chunk = WQ ? 2 * (lane >> 4) + h : h * 4 + (lane >> 4);
+        const int co = (chunk ^ rsw) * 16;
         uint4 af[MS];
 #pragma unroll
         for (int jm = 0; jm < MS; ++jm) af[jm] = *reinterpret_cast<const uint4*>(lb + jm * 16 * ROWB + co);
+        uint4 wop[NMAT * NSUB];
+#pragma unroll
+        for (int q = 0; q < NMAT * NSUB; ++q) {
+          if constexpr (WQ)
+            wop[q] = h == 0 ? widen_e4m3(w[q].x, w[q].y) : widen_e4m3(w[q].z, w[q].w);
+          else
+            wop[q] = w[q * 2 + h];
+        }
 #pragma unroll
         for (int jm = 0; jm < MS; ++jm)
 #pragma unroll
           for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int i = 0; i < NSUB; ++i) acc[m][i][jm] = mma16<Tr>(w[(m * NSUB + i) * 2 + h], af[jm], acc[m][i][jm]);
+            for (int i = 0; i < NSUB; ++i) acc[m][i][jm] = mma16<Tr>(wop[m * NSUB + i], af[jm], acc[m][i][jm]);
       }
     };
     // One iteration `it` (u = it mod NA, so stage and register indices are
@@ -275,6 +316,22 @@ struct Gemm {
     }
 
     // epilogue: lane holds rows n = n0 + 16 i + 4 (lane/16) + r of column m
+    // (fp8 weights: times the scale of channel n)
+    float sc[NMAT][NSUB][4];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i) {
+        const int n = c.n0 + i * 16 + (lane >> 4) * 4;
+        float4 v4 = float4{1.f, 1.f, 1.f, 1.f};
+        if constexpr (WQ) {
+          if (n < c.N) v4 = *reinterpret_cast<const float4*>(c.scale[m] + n);
+        }
+        sc[m][i][0] = v4.x;
+        sc[m][i][1] = v4.y;
+        sc[m][i][2] = v4.z;
+        sc[m][i][3] = v4.w;
+      }
 #pragma unroll
     for (int jm = 0; jm < MS; ++jm) {
       const int m = jm * 16 + (lane & 15);
@@ -287,7 +344,8 @@ struct Gemm {
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              v[r] = GATED ? silu_mul(acc[0][i][jm][r], acc[NMAT - 1][i][jm][r]) : acc[0][i][jm][r];
+              v[r] = GATED ? silu_mul(acc[0][i][jm][r] * sc[0][i][r], acc[NMAT - 1][i][jm][r] * sc[NMAT - 1][i][r])
+                           : acc[0][i][jm][r] * sc[0][i][r];
             store4<Tr>(orow + (size_t)n * sizeof(Elt), v[0], v[1], v[2], v[3]);
           }
         }
@@ -307,9 +365,9 @@ struct Gemm {
   }
 };
 
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int WAUX>
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int WAUX, bool WQ>
 __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) {
-  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, WAUX>;
+  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, WAUX, WQ>;
   // one LDS array per activation stage (stages past NA are 16-byte stubs)
   __shared__ __attribute__((aligned(16))) char st0[G::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[G::STAGE];
@@ -330,7 +388,7 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   // Skew test, identical in every workgroup: are some experts' tile counts
   // well above the mean over active experts (max * active > 2 * tiles)?
   bool skewed = false;
-  if (p.xcd_chunk > 0) {
+  if (p.skew_map) {
     int mx = 0, act = 0;
     for (int b = 0; b < p.E; b += 64) {
       const int i = b + lane;
@@ -340,6 +398,9 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+    // uniform by construction; saying so keeps the tile entry and the values
+    // derived from it in scalar registers
+    mx = __builtin_amdgcn_readfirstlane(mx);
     skewed = (long long)mx * act > 2LL * ntiles;
   }
   int L;
@@ -348,8 +409,7 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
     if (j >= J) return;
     L = (blockIdx.x & 7) * J + j;
   } else {
-    const int q = j / p.xcd_chunk;
-    L = ((q << 3) + (blockIdx.x & 7)) * p.xcd_chunk + (j - q * p.xcd_chunk);
+    L = ((j / kXcdChunk) * 8 + (blockIdx.x & 7)) * kXcdChunk + j % kXcdChunk;
   }
   if (L >= total) return;
   // expert e owns units [tile_off[e] * NT, tile_off[e+1] * NT)
@@ -393,8 +453,9 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
     c.act = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(reinterpret_cast<const char*>(p.act) + (size_t)ent.y * ld), (short)0, ent.z * ld, 0x00020000);
   }
-  const size_t wbase = (size_t)e * p.N * ld + (size_t)nbase * ld;
-  const int wbytes = min(G::BN, p.N - nbase) * ld;  // reads past N return 0 (column tail)
+  const int ldw = WQ ? p.K : ld;               // weight row bytes (one byte per fp8 code)
+  const size_t wbase = (size_t)e * p.N * ldw + (size_t)nbase * ldw;
+  const int wbytes = min(G::BN, p.N - nbase) * ldw;  // reads past N return 0 (column tail)
   c.w[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(reinterpret_cast<const char*>(p.w0) + wbase),
                                              (short)0, wbytes, 0x00020000);
   if (GATED)
@@ -402,29 +463,33 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
         const_cast<char*>(reinterpret_cast<const char*>(p.w1) + wbase), (short)0, wbytes, 0x00020000);
 #pragma unroll
   for (int i = 0; i < G::NSUB; ++i)
-    c.wlane[i] = ((wave % WN) * WTN + 16 * i + (lane & 15)) * ld + (lane >> 4) * 16;
+    c.wlane[i] = ((wave % WN) * WTN + 16 * i + (lane & 15)) * ldw + (lane >> 4) * 16;
+  if constexpr (WQ) {
+    c.scale[0] = p.s0 + (size_t)e * p.N;
+    c.scale[G::NMAT - 1] = (GATED ? p.s1 : p.s0) + (size_t)e * p.N;
+  }
   G::template run_ms<G::MSUB>((ent.z + 15) >> 4, c);
 }
 
-template <class Tr, class Cfg, bool GATED>
+template <class Tr, class Cfg, bool GATED, bool WQ>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   constexpr int BN = Cfg::WN * Cfg::WTN;
   const int NT = (a.N + BN - 1) / BN;
   const long long units = (long long)a.max_tiles * NT;
-  const long long round = a.xcd_chunk > 0 ? 8LL * a.xcd_chunk : 8;  // chunked mapping: whole rounds of chunks
+  const long long round = a.skew_map ? 8LL * kXcdChunk : 8;  // chunked mapping: whole rounds of chunks
   const long long grid = ((units + round - 1) / round) * round;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::WAUX>),
+  hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::WAUX, WQ>),
                      dim3((unsigned)grid), dim3(64 * Cfg::WN * Cfg::WK), 0, stream, a);
   return hipGetLastError();
 }
 
-template <class Tr, bool GATED>
+template <class Tr, bool GATED, bool WQ = false>
 hipError_t dispatch_bm(int BM, const GemmArgs& a, hipStream_t stream) {
   switch (BM) {
 #define MOE_BM_CASE(bm) \
   case bm:              \
-    return launch_cfg<Tr, typename TileCfg<bm, GATED>::type, GATED>(a, stream);
+    return launch_cfg<Tr, typename TileCfg<bm, GATED>::type, GATED, WQ>(a, stream);
     MOE_BM_CASE(16)
     MOE_BM_CASE(32)
     MOE_BM_CASE(48)

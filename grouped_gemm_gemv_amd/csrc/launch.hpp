@@ -68,21 +68,26 @@ struct GemmArgs {
   int act_nrows;             // rows of `act` when act_rows is set
   const void* w0;            // [E][N][K]
   const void* w1;            // [E][N][K] (gate+up: the up projection), else null
+  const float* s0;           // fp8 weights: [E][N] per-channel scales of w0, else null
+  const float* s1;           // fp8 weights: [E][N] per-channel scales of w1, else null
   void* out;                 // [R][N]
   const int32_t* tile_off;   // [E+1] of this pass
   const int32_t* tile_map;   // [max_tiles][4] of this pass
   const int32_t* n_tiles;    // [1] of this pass
   int E, K, N;
   int max_tiles;
-  int xcd_chunk;             // S > 0: uneven tile counts per expert deal chunks of S units to the XCDs in turn
+  int skew_map;              // 1: uneven tile counts per expert deal chunks of units to the XCDs in turn
 };
 
 hipError_t launch_gemm_bf16_gateup(int BM, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_bf16_down(int BM, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_f32_gateup(int BM, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_f32_down(int BM, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_fp8w_gateup(int BM, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_fp8w_down(int BM, const GemmArgs& a, hipStream_t stream);
 
 inline hipError_t launch_grouped_gemm(int dtype, bool gated, int BM, const GemmArgs& a, hipStream_t stream) {
+  if (a.s0 != nullptr) return gated ? launch_gemm_fp8w_gateup(BM, a, stream) : launch_gemm_fp8w_down(BM, a, stream);
   if (dtype == 1) return gated ? launch_gemm_bf16_gateup(BM, a, stream) : launch_gemm_bf16_down(BM, a, stream);
   return gated ? launch_gemm_f32_gateup(BM, a, stream) : launch_gemm_f32_down(BM, a, stream);
 }

@@ -210,6 +210,41 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
                          const void* w_up, const void* w_down, void* out, void* workspace,
                          size_t ws_bytes, moe_forward_views_t* views_out, hipStream_t stream);
 
+/* ---- fp8 expert weights ------------------------------------------------
+ * The TEMPO review (pith.science verdict for arXiv 2608.13057, referee
+ * summary and key machinery) measures the per-expert cost of an fp8 grouped
+ * GEMM: below its knee the time is HBM weight streaming, so storing the
+ * weights in 8 bits halves that regime's cost.  The pages fix neither the
+ * format nor the scale granularity; these entry points take OCP 8-bit
+ * floating point E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 is subnormal; S.1111.111 is NaN; no infinity) with
+ * one fp32 scale per output channel:
+ *   W[e, n, i] = scale[e, n] * e4m3(code[e, n, i]).
+ * Activations, h, y_perm and out stay bf16 (shape dtype must be MOE_BF16,
+ * else MOE_ERR_UNSUPPORTED); each code is widened exactly to bf16 in
+ * registers, products accumulate in fp32 and the channel scale multiplies
+ * the fp32 sum before SiLU / the final rounding.  Dispatch, workspace sizes
+ * (moe_query) and everything else are as for the bf16 entry points.  A NaN
+ * code propagates NaN to the outputs that use it. */
+
+/* moe_ffn_gate_up_gather with fp8 weights: w_gate, w_up [E,F,d] codes;
+ * s_gate, s_up [E,F] fp32 scales; x [T,d] read through disp->token_of. */
+moe_status_t moe_ffn_gate_up_fp8(const moe_shape_t* s, const void* x, const uint8_t* w_gate,
+                                 const uint8_t* w_up, const float* s_gate, const float* s_up,
+                                 const moe_dispatch_t* disp, int pass, void* h, hipStream_t stream);
+
+/* moe_ffn_down with fp8 weights: w_down [E,d,F] codes; s_down [E,d] scales. */
+moe_status_t moe_ffn_down_fp8(const moe_shape_t* s, const void* h, const uint8_t* w_down,
+                              const float* s_down, const moe_dispatch_t* disp, int pass,
+                              void* y_perm, hipStream_t stream);
+
+/* moe_forward with fp8 expert weights (the router stays in dtype). */
+moe_status_t moe_forward_fp8(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
+                             const int32_t* topk_ids_in, const float* topk_w_in, const uint8_t* w_gate,
+                             const uint8_t* w_up, const uint8_t* w_down, const float* s_gate,
+                             const float* s_up, const float* s_down, void* out, void* workspace,
+                             size_t ws_bytes, moe_forward_views_t* views_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

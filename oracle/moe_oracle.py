@@ -52,6 +52,53 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP 8-bit floating point E4M3 codes, from the format's definition.
+
+    Bit 7 is the sign, bits 6..3 the exponent field E (bias 7), bits 2..0 the
+    mantissa M.  E = 0: subnormal, (M / 8) * 2^-6.  E >= 1: (1 + M / 8) *
+    2^(E - 7).  E = 15 with M = 7 (0x7F, 0xFF) is NaN; there is no infinity, so
+    the largest finite magnitude is (1 + 6/8) * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = sign * mag
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+
+
+class Fp8Weights:
+    """Expert weights stored as E4M3 codes with one scale per output channel.
+
+    codes [E, N, K] uint8 and scales [E, N] fp32 stand for the matrices
+    W[e, n, i] = scales[e, n] * e4m3(codes[e, n, i]).  The pages name an fp8
+    grouped GEMM (TEMPO review, referee summary) without fixing the format or
+    the scale granularity; per-output-channel scaling is the reading taken.
+    """
+
+    def __init__(self, codes: np.ndarray, scales: np.ndarray):
+        self.codes = np.asarray(codes, dtype=np.uint8)
+        self.scales = np.asarray(scales, dtype=np.float32)
+        assert self.codes.ndim == 3 and self.scales.shape == self.codes.shape[:2]
+
+    @property
+    def shape(self):
+        return self.codes.shape
+
+    def expert(self, e: int) -> np.ndarray:
+        """W[e] in float64 (every product of a code value and an fp32 scale is exact)."""
+        return self.scales[e].astype(np.float64)[:, None] * e4m3_to_f64(self.codes[e])
+
+
+def widen_expert(w, e: int, dtype: str) -> np.ndarray:
+    """Weights of expert e in float64: stored values of `dtype`, or dequantised fp8."""
+    if isinstance(w, Fp8Weights):
+        return w.expert(e)
+    return to_f64(w[e], dtype)
+
+
 # ----------------------------------------------------------------------------
 # Step 1: routing
 # ----------------------------------------------------------------------------
@@ -288,7 +335,7 @@ def expert_outputs(x, wg, wu, wd, dtype: str, disp, ids) -> np.ndarray:
         if fs.size == 0:
             continue
         X = x64[fs // k]
-        Y = swiglu_ffn(X, to_f64(wg[e], dtype), to_f64(wu[e], dtype), to_f64(wd[e], dtype))
+        Y = swiglu_ffn(X, widen_expert(wg, e, dtype), widen_expert(wu, e, dtype), widen_expert(wd, e, dtype))
         y[disp["row_of"][fs]] = Y
     return y
 
@@ -351,7 +398,7 @@ def forward_tokens(x, wg, wu, wd, dtype: str, ids, w, tokens: Sequence[int]) -> 
         if not sel:
             continue
         X = np.stack([x64[i] for i, _ in sel])
-        Y = swiglu_ffn(X, to_f64(wg[e], dtype), to_f64(wu[e], dtype), to_f64(wd[e], dtype))
+        Y = swiglu_ffn(X, widen_expert(wg, e, dtype), widen_expert(wu, e, dtype), widen_expert(wd, e, dtype))
         for (i, j), yrow in zip(sel, Y):
             out[i] += w64[tokens[i], j] * yrow
     return out

@@ -394,3 +394,90 @@ def test_gini_closed_forms():
     # two-level: half the experts at a, half at b: G = (b-a) / (2 (a+b))
     a, b = 1.0, 3.0
     assert abs(O.gini(np.array([a] * 4 + [b] * 4)) - (b - a) / (2 * (a + b))) < 1e-15
+
+
+# ----------------------------------------------------------------------------
+# fp8 (OCP E4M3) expert weights
+# ----------------------------------------------------------------------------
+
+def test_e4m3_decode_format_values():
+    # values fixed by the OCP 8-bit floating point definition (E4M3, bias 7)
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+            0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0,
+            0xB8: -1.0, 0xFE: -448.0}
+    got = O.e4m3_to_f64(np.array(list(want), dtype=np.uint8))
+    assert got.tolist() == list(want.values())
+    assert np.signbit(O.e4m3_to_f64(np.array([0x80], np.uint8)))[0]
+    assert np.isnan(O.e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8))).all()
+    pos = O.e4m3_to_f64(np.arange(0, 0x7F, dtype=np.uint8))
+    assert (np.diff(pos) > 0).all()                      # positive codes are ordered
+    neg = O.e4m3_to_f64(np.arange(0x80, 0xFF, dtype=np.uint8))
+    assert np.array_equal(neg, -pos)
+
+
+def test_e4m3_decode_matches_torch():
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch without float8_e4m3fn")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_to_f64(codes)
+    fin = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(got), ~fin)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+def _fp8_pair(rng, E, N, K):
+    """fp8 weights and the same matrices built independently as bf16 bits.
+
+    Each value is sign * (1 + m/8) * 2^p (or 0); the row scale is 2^q.  The
+    code is written from the E4M3 bit layout (exponent field p - q + 7), the
+    bf16 bits from the bf16 layout, so neither side uses the oracle's decoder.
+    """
+    m = rng.integers(0, 8, size=(E, N, K))
+    p = rng.integers(-3, 4, size=(E, N, K))
+    s = rng.integers(0, 2, size=(E, N, K))
+    zero = rng.random((E, N, K)) < 0.05
+    q = rng.integers(-12, -4, size=(E, N))
+    ef = p + 7                                           # E4M3 exponent field of the code
+    codes = np.where(zero, 0, (s << 7) | (ef << 3) | m).astype(np.uint8)
+    scales = np.exp2(q).astype(np.float32)
+    eb = p + q[:, :, None] + 127                         # bf16 exponent field of the value
+    bits = np.where(zero, 0, (s << 15) | (eb << 7) | (m << 4)).astype(np.uint16)
+    return O.Fp8Weights(codes, scales), bits
+
+
+def test_fp8_forward_equals_bf16_on_same_values():
+    rng = np.random.default_rng(21)
+    T, d, E, F, k = 9, 32, 4, 48, 2
+    wg8, wgb = _fp8_pair(rng, E, F, d)
+    wu8, wub = _fp8_pair(rng, E, F, d)
+    wd8, wdb = _fp8_pair(rng, E, d, F)
+    x = (rng.standard_normal((T, d)) * 4).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)     # truncated: exact bf16 values
+    wr = (rng.standard_normal((E, d))).astype(np.float32)
+    wrb = (wr.view(np.uint32) >> 16).astype(np.uint16)
+    a = O.forward(xb, wrb, wg8, wu8, wd8, k, "bf16")
+    b = O.forward(xb, wrb, wgb, wub, wdb, k, "bf16")
+    assert np.array_equal(a["out"], b["out"])
+
+
+def test_fp8_scale_is_per_output_channel():
+    # codes 0x38 (1.0) everywhere: W[n, i] = scale[n]; for one token routed to
+    # expert 0 with weight 1, g_n = sg[n] * sum(x), u_n = su[n] * sum(x),
+    # y_o = sd[o] * sum_n silu(g_n) * u_n
+    d, F = 8, 6
+    sg = np.array([[0.5, 1.0, 2.0, 0.25, 1.5, 3.0]], np.float32)
+    su = np.array([[1.0, 0.5, 0.125, 2.0, 1.0, 0.75]], np.float32)
+    sd = np.arange(1, d + 1, dtype=np.float32)[None, :] / 8
+    one = lambda N, K: np.full((1, N, K), 0x38, np.uint8)
+    x = np.linspace(-1, 1.5, d).astype(np.float32)[None, :]
+    ids = np.zeros((1, 1), np.int32)
+    w = np.ones((1, 1), np.float32)
+    r = O.forward(x, np.zeros((1, d), np.float32), O.Fp8Weights(one(F, d), sg), O.Fp8Weights(one(F, d), su),
+                  O.Fp8Weights(one(d, F), sd), 1, "f32", topk_ids=ids, topk_w=w)
+    sx = float(x.astype(np.float64).sum())
+    g = sg[0].astype(np.float64) * sx
+    u = su[0].astype(np.float64) * sx
+    hsum = float(np.sum(g / (1 + np.exp(-g)) * u))
+    np.testing.assert_allclose(r["out"][0], sd[0].astype(np.float64) * hsum, rtol=1e-13)

@@ -58,3 +58,48 @@ def test_capacity_bias_reaches_gini_target(target):
     assert abs(g - target) <= 0.005
     d = O.dispatch(ids, wl.E, wl.capacity, 64)
     assert d["spill_counts"].sum() > 0
+
+
+def test_e4m3_encoder_round_trip_and_ties():
+    from oracle import moe_oracle as O
+    from workloads import gen
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.e4m3_to_f64(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(gen.e4m3_codes_from_f32(vals[fin].astype(np.float32)), codes[fin])
+    pos = vals[:0x7F]
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)  # exact in fp32
+    even = np.where(np.arange(0x7E) % 2 == 0, np.arange(0x7E), np.arange(1, 0x7F))
+    assert np.array_equal(gen.e4m3_codes_from_f32(mid), even)
+    assert np.array_equal(gen.e4m3_codes_from_f32(-mid), even | 0x80)
+    assert gen.e4m3_codes_from_f32(np.array([470.0, -1e9], np.float32)).tolist() == [0x7E, 0xFE]
+
+
+def test_e4m3_encoder_matches_torch():
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch without float8_e4m3fn")
+    from workloads import gen
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal(200000) * rng.choice([1e-3, 0.05, 1.0, 60.0], 200000)).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(gen.e4m3_codes_from_f32(v), ref)
+
+
+def test_fp8_workload_inputs():
+    from oracle import moe_oracle as O
+    wl = get_workload("mixtral_decode_t1_fp8")
+    assert wl.weights == "e4m3" and wl.dtype == "bf16"
+    # a small slice of the quantiser's contract on one expert row block
+    from workloads import gen
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    c, s = gen.quantize_rows_e4m3(w, block=16)
+    deq = s.astype(np.float64)[:, None] * O.e4m3_to_f64(c)
+    assert np.abs(c.view(np.int8)).max() <= 0x7E                  # no NaN codes
+    assert (np.abs(deq).max(axis=1) == s.astype(np.float64) * 448).all()  # row max maps to 448
+    # nearest rounding: within half a spacing, 2^-4 of the value in the normal
+    # range and 2^-10 of the scale (half the subnormal step 2^-9) below it
+    bound = 2.0 ** -4 * np.abs(w).astype(np.float64) + 2.0 ** -10 * s.astype(np.float64)[:, None]
+    assert (np.abs(deq - w) <= bound * (1 + 1e-6)).all()

@@ -34,6 +34,7 @@ class Workload:
     zipf_alpha: Optional[float] = None
     gini_target: Optional[float] = None
     bias_sigma: Optional[float] = None
+    weights: str = "dtype"  # expert weights: "dtype" (as x), or "e4m3" (OCP E4M3 codes + per-row fp32 scales)
 
     @property
     def rows(self) -> int:
@@ -51,9 +52,9 @@ class Workload:
 CAPACITY_BIAS_SIGMA = {0.10: 0.074219, 0.30: 0.238281}
 
 
-def _mixtral(T: int, name: str) -> Workload:
+def _mixtral(T: int, name: str, weights: str = "dtype") -> Workload:
     return Workload(name=name, T=T, d=4096, E=8, k=2, F=14336, dtype="bf16",
-                    x_std=1.0, wr_std=0.02, w_std=0.02, routing="router")
+                    x_std=1.0, wr_std=0.02, w_std=0.02, routing="router", weights=weights)
 
 
 def _build() -> Dict[str, Workload]:
@@ -77,6 +78,11 @@ def _build() -> Dict[str, Workload]:
                         capacity=384, gini_target=g, bias_sigma=CAPACITY_BIAS_SIGMA[g])
     # Compute-bound point at the Mixtral shape (at least 512 rows per expert).
     w["mixtral_t4096"] = _mixtral(4096, "mixtral_t4096")
+    # fp8 expert weights (E4M3 codes, one fp32 scale per output channel) at the
+    # Mixtral layer and decode sizes; the same fp32 draws as the bf16 workloads.
+    for T in (512, 1, 8, 32, 128, 256):
+        n = f"mixtral_t{T}_fp8" if T == 512 else f"mixtral_decode_t{T}_fp8"
+        w[n] = _mixtral(T, n, weights="e4m3")
     return w
 
 

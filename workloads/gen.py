@@ -63,6 +63,42 @@ class Inputs:
     wd: Optional[np.ndarray]           # [E, d, F]
     topk_ids: Optional[np.ndarray]     # [T, k] int32 (supplied routing), or None
     topk_w: Optional[np.ndarray]       # [T, k] fp32 (supplied routing), or None
+    sg: Optional[np.ndarray] = None    # [E, F] fp32 channel scales of wg (E4M3 weights), else None
+    su: Optional[np.ndarray] = None    # [E, F]
+    sd: Optional[np.ndarray] = None    # [E, d]
+
+
+def e4m3_codes_from_f32(v: np.ndarray) -> np.ndarray:
+    """OCP E4M3 codes of fp32 values: round to nearest, ties to even, saturating at +-448.
+
+    E4M3: sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+    holds the subnormals m * 2^-9.  Used to synthesise fp8 weight inputs (a
+    quantised checkpoint); the layer itself only reads codes.  Normal range:
+    the fp32 mantissa is rounded to 3 bits on the bit pattern (adding
+    0x7FFFF plus the lowest kept bit, then truncating, carries into the
+    exponent when the rounding does); subnormal range: m = rint(|v| * 512).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    sign = ((v.view(np.uint32) >> np.uint32(24)) & np.uint32(0x80)).astype(np.int32)
+    a = np.abs(v)
+    au = a.view(np.uint32)
+    r = au + np.uint32(0x7FFFF) + ((au >> np.uint32(20)) & np.uint32(1))
+    normal = (((r >> np.uint32(23)).astype(np.int32) - 120) << 3) | ((r >> np.uint32(20)) & np.uint32(7)).astype(np.int32)
+    sub = np.rint(np.minimum(a, np.float32(1.0)) * np.float32(512.0)).astype(np.int32)
+    code = np.where(au < np.uint32(0x3C800000), sub, normal)  # 0x3C800000 = 2^-6
+    return (np.minimum(code, 0x7E) | sign).astype(np.uint8)
+
+
+def quantize_rows_e4m3(w: np.ndarray, block: int = 512):
+    """Per-row (output channel) E4M3 quantisation of an fp32 matrix [N, K]:
+    scale[n] = max_i |w[n, i]| / 448 (fp32), codes = E4M3(w / scale)."""
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    codes = np.empty(w.shape, dtype=np.uint8)
+    for r0 in range(0, w.shape[0], block):
+        codes[r0:r0 + block] = e4m3_codes_from_f32(w[r0:r0 + block] / scale[r0:r0 + block, None])
+    return codes, scale
 
 
 def zipf_routing(T: int, E: int, k: int, alpha: float, seed: int):
@@ -111,7 +147,28 @@ def make_inputs(wl: Workload, seed: int = 0, experts: bool = True,
     if wl.routing == "zipf":
         ids, w = zipf_routing(T, wl.E, wl.k, wl.zipf_alpha, seed)
     wg = wu = wd = None
-    if experts:
+    sg = su = sd = None
+    if experts and wl.weights == "e4m3":
+        nthr = threads or min(16, os.cpu_count() or 1)
+        wg = np.empty((wl.E, wl.F, wl.d), dtype=np.uint8)
+        wu = np.empty((wl.E, wl.F, wl.d), dtype=np.uint8)
+        wd = np.empty((wl.E, wl.d, wl.F), dtype=np.uint8)
+        sg = np.empty((wl.E, wl.F), dtype=np.float32)
+        su = np.empty((wl.E, wl.F), dtype=np.float32)
+        sd = np.empty((wl.E, wl.d), dtype=np.float32)
+        dst = {_TAG_WG: (wg, sg), _TAG_WU: (wu, su), _TAG_WD: (wd, sd)}
+
+        def run_q(job):
+            tag, e, shape = job
+            c, sc = quantize_rows_e4m3(_normal(seed, tag, e, shape, wl.w_std, "f32"))
+            dst[tag][0][e] = c
+            dst[tag][1][e] = sc
+
+        jobs = [(t, e, (wl.d, wl.F) if t == _TAG_WD else (wl.F, wl.d))
+                for e in range(wl.E) for t in (_TAG_WG, _TAG_WU, _TAG_WD)]
+        with ThreadPoolExecutor(nthr) as ex:
+            list(ex.map(run_q, jobs))
+    elif experts:
         nthr = threads or min(16, os.cpu_count() or 1)
         jobs = []
         for e in range(wl.E):
@@ -130,4 +187,4 @@ def make_inputs(wl: Workload, seed: int = 0, experts: bool = True,
 
         with ThreadPoolExecutor(nthr) as ex:
             list(ex.map(run, jobs))
-    return Inputs(x=x, wr=wr, bias=bias, wg=wg, wu=wu, wd=wd, topk_ids=ids, topk_w=w)
+    return Inputs(x=x, wr=wr, bias=bias, wg=wg, wu=wu, wd=wd, topk_ids=ids, topk_w=w, sg=sg, su=su, sd=sd)
