@@ -60,7 +60,8 @@ def parse():
 
 
 GEMM_SOURCES = ["grouped_gemm.hpp", "gemm_tiles.hpp", "device_common.hpp"]
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "gateup_mixtral_t512_pmc.txt")
+def pmc_summary_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"gateup_{workload}_pmc.txt")
 
 
 def gemm_source_hash() -> str:
@@ -76,10 +77,11 @@ def gemm_source_hash() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch of the fused gate+up GEMM from the committed PMC summary,
     if it was taken on the current GEMM sources and this workload; else None."""
-    if not os.path.exists(PMC_SUMMARY):
+    path = pmc_summary_path(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PMC_SUMMARY):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -259,13 +261,22 @@ def cost_curve(args):
 
 
 def gemm_work(wl, counts, dt_bytes):
-    """Algorithmic FLOPs and HBM bytes of the two grouped GEMMs (per launch)."""
+    """Algorithmic FLOPs and HBM bytes of the two grouped GEMMs (per launch):
+    every active expert's weights once (E4M3 codes: 1 byte per element plus
+    one fp32 scale per output channel), activation rows read once per slot,
+    outputs written once."""
     Tk = wl.T * wl.k
     active = int((counts > 0).sum())
     gu_flops = 4.0 * Tk * wl.d * wl.F
     dn_flops = 2.0 * Tk * wl.d * wl.F
-    gu_bytes = (active * 2.0 * wl.F * wl.d + Tk * wl.d + Tk * wl.F) * dt_bytes  # x rows read once per slot
-    dn_bytes = (active * 1.0 * wl.F * wl.d + Tk * wl.F + Tk * wl.d) * dt_bytes
+    if wl.weights == "e4m3":
+        wgu = active * (2.0 * wl.F * wl.d + 2.0 * wl.F * 4)
+        wdn = active * (1.0 * wl.F * wl.d + wl.d * 4)
+    else:
+        wgu = active * 2.0 * wl.F * wl.d * dt_bytes
+        wdn = active * 1.0 * wl.F * wl.d * dt_bytes
+    gu_bytes = wgu + (Tk * wl.d + Tk * wl.F) * dt_bytes
+    dn_bytes = wdn + (Tk * wl.F + Tk * wl.d) * dt_bytes
     return gu_flops, gu_bytes, dn_flops, dn_bytes, active
 
 
@@ -276,16 +287,19 @@ def cpu_baseline(wl, inp, sample_tokens):
 
     from oracle import moe_oracle as O
     n = wl.T if sample_tokens <= 0 else min(wl.T, sample_tokens)
+    wg, wu, wd = inp.wg, inp.wu, inp.wd
+    if wl.weights == "e4m3":
+        wg, wu, wd = O.Fp8Weights(inp.wg, inp.sg), O.Fp8Weights(inp.wu, inp.su), O.Fp8Weights(inp.wd, inp.sd)
     cores = min(16, os.cpu_count() or 1)
     reps, total = 0, 0.0
     with threadpool_limits(limits=cores):
         while reps == 0 or (total < 10.0 and reps < 5):
             t0 = time.perf_counter()
             if inp.topk_ids is None:
-                O.forward(inp.x[:n], inp.wr, inp.wg, inp.wu, inp.wd, wl.k, wl.dtype, bias=inp.bias,
+                O.forward(inp.x[:n], inp.wr, wg, wu, wd, wl.k, wl.dtype, bias=inp.bias,
                           capacity=wl.capacity)
             else:
-                O.forward(inp.x[:n], inp.wr, inp.wg, inp.wu, inp.wd, wl.k, wl.dtype,
+                O.forward(inp.x[:n], inp.wr, wg, wu, wd, wl.k, wl.dtype,
                           topk_ids=inp.topk_ids[:n], topk_w=inp.topk_w[:n], capacity=wl.capacity)
             total += time.perf_counter() - t0
             reps += 1
@@ -344,6 +358,8 @@ def main():
 
     x, wr, bias = dev(inp.x), dev(inp.wr), dev(inp.bias)
     wg, wu, wd = dev(inp.wg), dev(inp.wu), dev(inp.wd)
+    fp8 = wl.weights == "e4m3"
+    sg, su, sd = dev(inp.sg), dev(inp.su), dev(inp.sd)
     ids_in, w_in = dev(inp.topk_ids), dev(inp.topk_w)
     shape = M.Shape(wl.T, wl.d, wl.E, wl.k, wl.F, wl.capacity, dt)
     q = M.query(shape)
@@ -351,6 +367,8 @@ def main():
     out = torch.empty((wl.T, wl.d), dtype=dt, device="cuda")
 
     def step():
+        if fp8:
+            return M.moe_forward_fp8(shape, x, wr, bias, ids_in, w_in, wg, wu, wd, sg, su, sd, out, ws)
         return M.moe_forward(shape, x, wr, bias, ids_in, w_in, wg, wu, wd, out, ws)
 
     views = step()
@@ -409,8 +427,14 @@ def main():
     it = args.kernel_iters
     passes = q.n_passes
     # the gate+up kernel exactly as moe_forward runs it (gather folded into its loads)
-    t_gu = sum(timed(lambda p=p: M.moe_ffn_gate_up_gather(shape, x, wg, wu, disp, p, h), it) for p in range(passes))
-    t_dn = sum(timed(lambda p=p: M.moe_ffn_down(shape, h, wd, disp, p, y), it) for p in range(passes))
+    if fp8:
+        t_gu = sum(timed(lambda p=p: M.moe_ffn_gate_up_fp8(shape, x, wg, wu, sg, su, disp, p, h), it)
+                   for p in range(passes))
+        t_dn = sum(timed(lambda p=p: M.moe_ffn_down_fp8(shape, h, wd, sd, disp, p, y), it) for p in range(passes))
+    else:
+        t_gu = sum(timed(lambda p=p: M.moe_ffn_gate_up_gather(shape, x, wg, wu, disp, p, h), it)
+                   for p in range(passes))
+        t_dn = sum(timed(lambda p=p: M.moe_ffn_down(shape, h, wd, disp, p, y), it) for p in range(passes))
     t_perm = timed(lambda: M.moe_permute(shape, x, ids, disp, xp, pws), it)
     t_comb = timed(lambda: M.moe_combine(shape, y, wts, disp, out), it)
     t_route = 0.0
@@ -432,7 +456,7 @@ def main():
         ach = gu_flops / (t_gu * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_f, "unit": "TFLOP/s",
                 "frac": round(ach / peak_f, 4), "traffic": measured_traffic(wl.name)}
-    roof["kernel"] = "grouped_gemm_kernel (fused gate+up SwiGLU)"
+    roof["kernel"] = "grouped_gemm_kernel (fused gate+up SwiGLU%s)" % (", E4M3 weights" if fp8 else "")
     roof["gemm_source_sha"] = gemm_source_hash()
     roof["us_per_launch"] = round(t_gu / passes, 2)
     roof["algorithmic_bytes"] = gu_bytes
@@ -464,7 +488,8 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded normal draws, random-init weights)",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "F": wl.F,
-                   "capacity": wl.capacity, "seed": args.seed, "graph": True},
+                   "capacity": wl.capacity, "seed": args.seed, "graph": True,
+                   "expert_weights": "e4m3 codes + fp32 channel scales" if fp8 else wl.dtype},
         "grouped_gemm": gg,
         "per_call_us": {"route": round(t_route, 1), "permute": round(t_perm, 1), "gate_up": round(t_gu, 1),
                         "down": round(t_dn, 1), "combine": round(t_comb, 1)},
