@@ -19,16 +19,21 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest row-tile height of the grouped GEMMs.  A tile holds up to BM rows
 // and only its non-empty 16-row subtiles are computed, so a tall tile costs
-// nothing for short experts.  The tall configurations (BM 160/192: 112- or
-// 128-column workgroups, K not split) stream weights best and give a hot
-// expert the fewest row tiles, but need enough column tiles to occupy every
-// compute unit: they are used when the down projection alone has at least
-// one 128-column tile per compute unit over the experts that can be active.
-// BM 160 is the 112-column gate+up tile, used when 112 divides F and the
-// mean expert fits in it.  Otherwise (few active experts, decode) the tile
-// covers an active expert's rows with one tile (1.25x the mean of T*k over
-// min(E, T*k) experts, at most C in the capacity pass), and the short
-// configurations split K across wavefronts so that there are enough units.
+// nothing for short experts.  The configurations come in two families:
+//  * tall (BM 160/192: 112- or 128-column workgroups, K not split) stream
+//    weights best and give a hot expert the fewest row tiles, but need many
+//    column tiles to occupy the 256 compute units;
+//  * short (BM 16/32: 32 columns, K split over 4 wavefronts; BM 48/64: 64
+//    columns, K split over 2) multiply the workgroups without duplicating a
+//    weight stream, for few active experts.
+// Measured rule (per-expert cost curves at the Mixtral and 64-expert shapes):
+// tall when the down projection has at least 192 tiles of 128 columns over
+// the experts that can be active, or when experts average more than 64 rows
+// and there are at least 64 such tiles; otherwise 64 rows for experts past 32
+// rows, 48 when 64-column tiles alone fill the chip, else the smallest of
+// 16/32 holding 1.25x the mean.  BM 160 is the 112-column gate+up tile, used
+// when 112 divides F and the mean expert fits in it.  The mean is T*k over
+// min(E, T*k) experts, at most C in the capacity pass.
 constexpr int kTileRows[] = {16, 32, 48, 64, 96, 128, 160, 192};
 constexpr int kComputeUnits = 256;
 
@@ -44,11 +49,12 @@ int choose_tile_rows(const moe_shape_t& s) {
   const int64_t active = std::min<int64_t>(s.E, Tk);
   int64_t mean = ceil_div(Tk, active);
   if (s.capacity > 0) mean = std::min<int64_t>(mean, s.capacity);
-  if (active * ceil_div(s.d, 128) >= kComputeUnits) return (mean <= 160 && s.F % 112 == 0) ? 160 : 192;
-  const int64_t want = std::max<int64_t>(mean, (mean * 5 + 3) / 4);
-  for (int v : kTileRows)
-    if (v >= want) return v;
-  return kTileRows[sizeof(kTileRows) / sizeof(kTileRows[0]) - 1];
+  const int64_t tall_tiles = active * ceil_div(s.d, 128);
+  if (tall_tiles >= kComputeUnits * 3 / 4 || (mean > 64 && tall_tiles >= 64) || mean > 128)
+    return (mean <= 160 && s.F % 112 == 0) ? 160 : 192;
+  if (mean > 32) return 64;
+  if (active * ceil_div(s.d, 64) >= kComputeUnits) return 48;
+  return (mean * 5 + 3) / 4 <= 16 ? 16 : 32;
 }
 
 int64_t spill_bound(const moe_shape_t& s) { return std::max<int64_t>(0, (int64_t)s.T * s.k - s.capacity); }

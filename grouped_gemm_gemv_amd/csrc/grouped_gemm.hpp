@@ -287,7 +287,14 @@ struct Gemm {
       constexpr int PART = NMAT * NSUB * MS * 4 * 64;  // floats per wavefront partial
       // wavefront column wn reduces through LDS stage wn
       static_assert((size_t)PART * sizeof(float) <= (size_t)STAGE && WN <= NA, "LDS too small for split-K");
-      float* red = reinterpret_cast<float*>(c.stage[(threadIdx.x >> 6) % WN]);
+      // (select with static indices: a run-time index into c.stage would put
+      // the whole context in scratch memory)
+      const int wn = (threadIdx.x >> 6) % WN;
+      char* redb = c.stage[0];
+#pragma unroll
+      for (int i = 1; i < WN; ++i)
+        if (wn == i) redb = c.stage[i];
+      float* red = reinterpret_cast<float*>(redb);
       for (int src = 1; src < WK; ++src) {
         if (c.wk == src) {
 #pragma unroll

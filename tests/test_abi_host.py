@@ -90,6 +90,20 @@ def test_automatic_tile_rows(name, bm):
     assert st == 0 and q.tile_rows == bm
 
 
+@pytest.mark.parametrize("T,E,k,d,F,bm", [
+    (16, 1, 1, 4096, 14336, 32),    # one expert, 16 rows: split-K 32-row tiles
+    (64, 1, 1, 4096, 14336, 64),    # past 32 rows: 64-row split-K tiles
+    (128, 1, 1, 4096, 14336, 64),   # 32 tall down tiles only: stay short
+    (256, 1, 1, 4096, 14336, 192),  # past 128 rows: tall
+    (256, 2, 1, 4096, 14336, 160),  # 128 rows, 64 tall down tiles: tall
+    (128, 8, 1, 2048, 1408, 48),    # 16 rows, 8 x 32 64-column tiles fill the chip
+    (256, 8, 2, 3584, 2560, 192),   # 224 tall down tiles >= 192
+])
+def test_tile_rows_rule_shapes(T, E, k, d, F, bm):
+    st, q = _query(_shape(T=T, d=d, E=E, k=k, F=F))
+    assert st == 0 and q.tile_rows == bm
+
+
 def test_capacity_rows_example():
     st, q = _query(_shape(T=4096, d=2048, E=64, k=6, F=1408, C=384))
     assert st == 0 and q.rows == 64 * 384 + (4096 * 6 - 384)
