@@ -401,6 +401,16 @@ def main():
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / args.steps
     log(f"{args.steps} graph replays: {ms * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step)")
+    # spread: the same replays timed one by one (events around each replay)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    spread = {"p10": round(float(np.percentile(per, 10)), 4), "p50": round(float(np.median(per)), 4),
+              "p90": round(float(np.percentile(per, 90)), 4)}
 
     # per-call times (HIP events on the stream the kernels run on)
     cur = torch.cuda.current_stream()
@@ -482,6 +492,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_single_replays": spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -253,16 +253,23 @@ struct Gemm {
     //   3. issue the activation tile of it + PF into that free stage;
     //   4. MFMAs of iteration `it`;
     //   5. issue the weights of it + PF into the registers freed last iteration.
+    // The gate+up kernel raises the wavefront's issue priority while it issues
+    // loads, so a wavefront busy with MFMAs on the same SIMD does not delay the
+    // next loads (measured 1.5 % at 128 rows per expert; no gain for down).
     auto body = [&](int it, auto uc) {
       constexpr int u = decltype(uc)::value;
       wait_vm<WAITN>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if constexpr (GATED) __builtin_amdgcn_s_setprio(2);
       load_a(it + PF, c.stage[(u + PF) % NA]);
+      if constexpr (GATED) __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       if (WK == 1 || it * WK + c.wk < c.nk) compute(c.stage[u], wq[u]);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (GATED) __builtin_amdgcn_s_setprio(2);
       load_w(it + PF, wq[(u + PF) % NA]);
+      if constexpr (GATED) __builtin_amdgcn_s_setprio(0);
     };
 
 #pragma unroll

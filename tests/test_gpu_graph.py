@@ -69,3 +69,48 @@ def test_graph_replays_match_eager(base, over):
         junk = torch.randn(1 << 20, device="cuda").sum()
         torch.cuda.synchronize()
         assert torch.isfinite(junk)
+
+
+def test_graph_replays_match_eager_fp8():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_gemm_gemv_amd as M
+    wl = get_workload("mixtral_t512_fp8", T=200, d=256, F=320)
+    inp = make_inputs(wl, 0)
+    inp2 = make_inputs(wl, 1, experts=False)
+    shape = M.Shape(wl.T, wl.d, wl.E, wl.k, wl.F, 0, torch.bfloat16)
+    q = M.query(shape)
+    x = dev(inp.x)
+    xs = [dev(inp.x), dev(inp2.x)]
+    wr = dev(inp.wr)
+    wts = [dev(getattr(inp, n)) for n in ("wg", "wu", "wd", "sg", "su", "sd")]
+    ws = M.workspace(q.forward_ws_bytes)
+    out = torch.empty((wl.T, wl.d), dtype=torch.bfloat16, device="cuda")
+    ws_e = M.workspace(q.forward_ws_bytes)
+    refs = []
+    for xi in xs:
+        o = torch.empty_like(out)
+        M.moe_forward_fp8(shape, xi, wr, None, None, None, *wts, o, ws_e)
+        torch.cuda.synchronize()
+        refs.append(bits(o))
+
+    def step():
+        M.moe_forward_fp8(shape, x, wr, None, None, None, *wts, out, ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        which = rep % 2
+        x.copy_(xs[which])
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), refs[which]), f"replay {rep} differs"

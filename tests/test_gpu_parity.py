@@ -43,6 +43,13 @@ CASES = {
     "bf16_bm128": ("mixtral_t512", dict(T=400, d=128, F=256)),
     "bf16_bm160": ("mixtral_t512", dict(T=512, d=256, F=128)),
     "bf16_bm192": ("mixtral_t512", dict(T=512, d=128, E=4, F=192)),
+    # degenerate and extreme cases: no overflow region at all (C = T*k), one
+    # entry per expert in the fixed region (C = 1), every entry routed to one
+    # expert (k = 1, Zipf with an overwhelming first rank), the largest E and k
+    "bf16_cap_no_spill": ("capacity_gini0.30", dict(T=64, d=128, E=8, k=2, F=128, capacity=128)),
+    "bf16_cap_c1": ("capacity_gini0.30", dict(T=100, d=64, E=8, k=2, F=64, capacity=1)),
+    "bf16_one_expert": ("e64_zipf_a2.0", dict(T=300, d=128, E=16, k=1, F=128, zipf_alpha=60.0)),
+    "bf16_e256_k64": ("mixtral_t512", dict(T=33, d=64, E=256, k=64, F=64)),
 }
 
 
@@ -123,6 +130,15 @@ def test_route(runs, case):
 def test_dispatch_bit_exact(runs, case):
     r = runs(case)
     check_dispatch(r.disp.arrays(), r.ref_disp, r.wl.E)
+
+
+def test_degenerate_cases_are_what_they_claim(runs):
+    r = runs("bf16_cap_no_spill")
+    assert r.ref_disp["spill_counts"].sum() == 0 and O.spill_rows_bound(64, 2, 128) == 0
+    r = runs("bf16_one_expert")
+    assert len(np.unique(r.gpu_ids)) == 1
+    r = runs("bf16_cap_c1")
+    assert (r.ref_disp["kept_counts"] <= 1).all() and r.ref_disp["spill_counts"].sum() > 0
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
