@@ -37,14 +37,16 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the GPU raises its clocks over the first tens of milliseconds of load:
+    # the default warm-up (about 0.1 s of replays) reaches the steady state
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", default="mixtral_t512")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the workload the CPU oracle runs (0: all)")
-    ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--kernel-iters", type=int, default=40)
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first copy 256 MiB device to device 3 times (reference for PMC byte counters)")
     ap.add_argument("--summarize", metavar="DB", help="print a text summary of a rocprofv3 result database and exit")
@@ -401,16 +403,6 @@ def main():
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / args.steps
     log(f"{args.steps} graph replays: {ms * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step)")
-    # spread: the same replays timed one by one (events around each replay)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:
-        a.record()
-        g.replay()
-        b.record()
-    torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) for a, b in evs])
-    spread = {"p10": round(float(np.percentile(per, 10)), 4), "p50": round(float(np.median(per)), 4),
-              "p90": round(float(np.percentile(per, 90)), 4)}
 
     # per-call times (HIP events on the stream the kernels run on)
     cur = torch.cuda.current_stream()
@@ -422,7 +414,7 @@ def main():
     wts = views.topk_w
 
     def timed(fn, iters):
-        for _ in range(3):
+        for _ in range(10):
             fn()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
@@ -454,6 +446,17 @@ def main():
         t_route = timed(lambda: M.moe_route(shape, x, wr, bias, rid, rw), it)
     log(f"per call (us): route {t_route:.1f} permute {t_perm:.1f} gate_up {t_gu:.1f} down {t_dn:.1f} "
         f"combine {t_comb:.1f}")
+    # spread: the same replays timed one by one (events around each replay)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    spread = {"p10": round(float(np.percentile(per, 10)), 4), "p50": round(float(np.median(per)), 4),
+              "p90": round(float(np.percentile(per, 90)), 4)}
+
 
     gu_flops, gu_bytes, dn_flops, dn_bytes, active = gemm_work(wl, counts, dt_bytes)
     peak_f = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
