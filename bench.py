@@ -1,6 +1,6 @@
 """Benchmark of the MoE layer forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral_t512]
+    python bench.py [--gpus 1] [--steps K=200] [--warmup W=150] [--workload mixtral_t512]
 
 A step is one whole layer (routing, count/scan, permutation, fused gate+up
 SwiGLU grouped GEMM, down grouped GEMM, combine) over one batch of seeded
