@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the workload the CPU oracle runs (0: all)")
     ap.add_argument("--kernel-iters", type=int, default=40)
+    ap.add_argument("--weight-layout", choices=("blocked16", "rows"), default="blocked16",
+                    help="storage order of the expert weights (re-stored once before timing)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first copy 256 MiB device to device 3 times (reference for PMC byte counters)")
     ap.add_argument("--summarize", metavar="DB", help="print a text summary of a rocprofv3 result database and exit")
@@ -363,7 +365,13 @@ def main():
     fp8 = wl.weights == "e4m3"
     sg, su, sd = dev(inp.sg), dev(inp.su), dev(inp.sd)
     ids_in, w_in = dev(inp.topk_ids), dev(inp.topk_w)
-    shape = M.Shape(wl.T, wl.d, wl.E, wl.k, wl.F, wl.capacity, dt)
+    blocked = args.weight_layout == "blocked16"
+    if blocked:
+        # weights are re-stored once, as a loader would; not part of a step
+        wg, wu, wd = M.moe_pack_blocked16(wg), M.moe_pack_blocked16(wu), M.moe_pack_blocked16(wd)
+        torch.cuda.synchronize()
+    shape = M.Shape(wl.T, wl.d, wl.E, wl.k, wl.F, wl.capacity, dt, 0,
+                    M.LAYOUT_BLOCKED16 if blocked else M.LAYOUT_ROWS)
     q = M.query(shape)
     ws = M.workspace(q.forward_ws_bytes)
     out = torch.empty((wl.T, wl.d), dtype=dt, device="cuda")
@@ -503,7 +511,8 @@ def main():
         "data": "synthetic (seeded normal draws, random-init weights)",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "F": wl.F,
                    "capacity": wl.capacity, "seed": args.seed, "graph": True,
-                   "expert_weights": "e4m3 codes + fp32 channel scales" if fp8 else wl.dtype},
+                   "expert_weights": "e4m3 codes + fp32 channel scales" if fp8 else wl.dtype,
+                   "weight_layout": args.weight_layout},
         "grouped_gemm": gg,
         "per_call_us": {"route": round(t_route, 1), "permute": round(t_perm, 1), "gate_up": round(t_gu, 1),
                         "down": round(t_dn, 1), "combine": round(t_comb, 1)},

@@ -12,6 +12,9 @@ from .api import (
     moe_ffn_down_fp8,
     moe_ffn_gate_up_fp8,
     moe_forward_fp8,
+    moe_pack_blocked16,
+    LAYOUT_ROWS,
+    LAYOUT_BLOCKED16,
     moe_ffn_gate_up,
     moe_ffn_gate_up_gather,
     moe_forward,
@@ -24,6 +27,7 @@ from .api import (
 
 __all__ = [
     "Dispatch", "ForwardViews", "Shape", "moe_combine", "moe_ffn_down", "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_forward",
-    "moe_ffn_gate_up_fp8", "moe_ffn_down_fp8", "moe_forward_fp8",
+    "moe_ffn_gate_up_fp8", "moe_ffn_down_fp8", "moe_forward_fp8", "moe_pack_blocked16",
+    "LAYOUT_ROWS", "LAYOUT_BLOCKED16",
     "moe_grouped_ffn", "moe_permute", "moe_route", "query", "workspace",
 ]

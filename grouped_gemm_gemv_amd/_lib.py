@@ -32,13 +32,13 @@ STATUS = {
 EXPORTED = [
     "moe_status_string", "moe_query", "moe_dispatch_carve", "moe_route", "moe_permute",
     "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_grouped_ffn", "moe_combine",
-    "moe_forward", "moe_ffn_gate_up_fp8", "moe_ffn_down_fp8", "moe_forward_fp8",
+    "moe_forward", "moe_ffn_gate_up_fp8", "moe_ffn_down_fp8", "moe_forward_fp8", "moe_pack_blocked16",
 ]
 
 
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", c_i32), ("d", c_i32), ("E", c_i32), ("k", c_i32), ("F", c_i32),
-                ("capacity", c_i32), ("dtype", c_i32), ("tile_rows", c_i32)]
+                ("capacity", c_i32), ("dtype", c_i32), ("tile_rows", c_i32), ("weight_layout", c_i32)]
 
 
 class MoeSizes(ctypes.Structure):
@@ -92,6 +92,7 @@ def _declare(lib):
         "moe_ffn_down_fp8": [S, c_ptr, c_ptr, c_ptr, D, ctypes.c_int, c_ptr, c_ptr],
         "moe_forward_fp8": [S, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                             c_ptr, c_ptr, ctypes.c_size_t, P(MoeForwardViews), c_ptr],
+        "moe_pack_blocked16": [c_ptr, c_ptr, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, c_ptr],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -30,9 +30,11 @@ class Shape:
     capacity: int = 0
     dtype: torch.dtype = torch.bfloat16
     tile_rows: int = 0  # 0: the library chooses
+    weight_layout: int = 0  # 0: row-major expert weights; 1: blocked 16-row order (moe_pack_blocked16)
 
     def c(self) -> MoeShape:
-        return MoeShape(self.T, self.d, self.E, self.k, self.F, self.capacity, _DT[self.dtype], self.tile_rows)
+        return MoeShape(self.T, self.d, self.E, self.k, self.F, self.capacity, _DT[self.dtype], self.tile_rows,
+                        self.weight_layout)
 
 
 def _p(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -121,6 +123,25 @@ def moe_ffn_gate_up_gather(shape: Shape, x, w_gate, w_up, disp: Dispatch, pass_i
     check("moe_ffn_gate_up_gather", lib().moe_ffn_gate_up_gather(
         ctypes.byref(shape.c()), _p(x), _p(w_gate), _p(w_up), ctypes.byref(disp.c), pass_idx, _p(h),
         _stream(stream)))
+
+
+LAYOUT_ROWS = 0
+LAYOUT_BLOCKED16 = 1
+
+
+def moe_pack_blocked16(src, dst=None, stream=None):
+    """Re-store a [..., rows, K] weight tensor (rows % 16 == 0, K * itemsize % 64 == 0)
+    in the blocked 16-row order; returns dst (allocated like src if None)."""
+    if dst is None:
+        dst = torch.empty_like(src)
+    if src.shape != dst.shape or src.dtype != dst.dtype:
+        raise ValueError("dst must match src")
+    rows = src.shape[-2]
+    row_bytes = src.shape[-1] * src.element_size()
+    matrices = src.numel() // (src.shape[-1] * rows)
+    check("moe_pack_blocked16", lib().moe_pack_blocked16(_p(src), _p(dst), matrices, rows, row_bytes,
+                                                         _stream(stream)))
+    return dst
 
 
 def moe_ffn_gate_up_fp8(shape: Shape, x, w_gate, w_up, s_gate, s_up, disp: Dispatch, pass_idx: int, h,

@@ -90,6 +90,7 @@ moe_status_t validate(const moe_shape_t* s) {
     return MOE_ERR_INVALID_ARG;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (s->tile_rows != 0 && !supported_tile_rows(s->tile_rows)) return MOE_ERR_UNSUPPORTED;
+  if (s->weight_layout != MOE_LAYOUT_ROWS && s->weight_layout != MOE_LAYOUT_BLOCKED16) return MOE_ERR_INVALID_ARG;
   if (s->d % 64 != 0 || s->F % 64 != 0) return MOE_ERR_UNSUPPORTED;
   const int64_t Tk = (int64_t)s->T * s->k;
   if (Tk >= INT32_MAX) return MOE_ERR_INVALID_ARG;
@@ -255,6 +256,7 @@ moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass,
   a.N = gated ? s.F : s.d;
   a.max_tiles = (int)pass_max_tiles(s, d.tile_rows, pass);
   a.skew_map = 1;
+  a.blocked16 = s.weight_layout == MOE_LAYOUT_BLOCKED16 ? 1 : 0;
   return a;
 }
 
@@ -457,6 +459,20 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
                          moe_forward_views_t* views_out, hipStream_t stream) {
   return forward_impl(s, x, w_router, bias, topk_ids_in, topk_w_in, w_gate, w_up, w_down, nullptr, nullptr,
                       nullptr, out, workspace, ws_bytes, views_out, stream);
+}
+
+moe_status_t moe_pack_blocked16(const void* src, void* dst, int64_t matrices, int64_t rows, int64_t row_bytes,
+                                hipStream_t stream) {
+  if (!src || !dst) return MOE_ERR_NULL_PTR;
+  if (matrices < 1 || rows < 16 || rows % 16 != 0 || row_bytes < 64 || row_bytes % 64 != 0)
+    return MOE_ERR_INVALID_ARG;
+  const int64_t bytes = matrices * rows * row_bytes;
+  const char* a = static_cast<const char*>(src);
+  const char* b = static_cast<const char*>(dst);
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlap
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_pack_blocked16(src, dst, matrices * rows / 16, row_bytes, stream));
 }
 
 moe_status_t moe_ffn_gate_up_fp8(const moe_shape_t* s, const void* x, const uint8_t* w_gate, const uint8_t* w_up,

@@ -118,6 +118,7 @@ struct Gemm {
     const int32_t* arow;             // null, or source row of each tile row (gather folded into the loads)
     __amdgpu_buffer_rsrc_t w[NMAT];  // this workgroup's weight rows (reads past N return 0)
     int wlane[NSUB];                 // byte offset of this lane's weight row/chunk per subtile
+    int wstep, whalf;                // weight bytes between K steps / between the two halves of a step
     const float* scale[NMAT];        // fp8 weights: per-channel scales of this expert
     char* out;                       // output row0
     char* stage[NA];                 // one LDS array per activation stage
@@ -190,7 +191,7 @@ struct Gemm {
 #pragma unroll
           for (int i = 0; i < NSUB; ++i)
             dst[m * NSUB + i] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * KWB, WAUX));
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * c.wstep, WAUX));
       } else {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -199,7 +200,7 @@ struct Gemm {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
               dst[(m * NSUB + i) * 2 + h] = __builtin_bit_cast(
-                  uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * kKB + h * 64, WAUX));
+                  uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * c.wstep + h * c.whalf, WAUX));
       }
     };
     // activation tile of iteration `it` into LDS stage `st`; past the last
@@ -475,9 +476,15 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   if (GATED)
     c.w[G::NMAT - 1] = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(reinterpret_cast<const char*>(p.w1) + wbase), (short)0, wbytes, 0x00020000);
+  // row-major: lane reads row (lane % 16) of the subtile, 16 bytes at
+  // 16 (lane / 16) of each 64-byte half step.  Blocked 16-row order: the
+  // same bytes sit at row * 64 inside the 1024-byte block of that half step.
+  const int rowpitch = p.blocked16 ? 64 : ldw;
+  c.wstep = p.blocked16 ? 16 * G::KWB : G::KWB;
+  c.whalf = p.blocked16 ? 1024 : 64;
 #pragma unroll
   for (int i = 0; i < G::NSUB; ++i)
-    c.wlane[i] = ((wave % WN) * WTN + 16 * i + (lane & 15)) * ldw + (lane >> 4) * 16;
+    c.wlane[i] = ((wave % WN) * WTN + 16 * i) * ldw + (lane & 15) * rowpitch + (lane >> 4) * 16;
   if constexpr (WQ) {
     c.scale[0] = p.s0 + (size_t)e * p.N;
     c.scale[G::NMAT - 1] = (GATED ? p.s1 : p.s0) + (size_t)e * p.N;

@@ -59,6 +59,10 @@ hipError_t launch_scatter(const int32_t* ids, int Tk, int k, int E, int C, int n
 hipError_t launch_gather(const void* x, const int32_t* row_of, int Tk, int k, int64_t row_bytes,
                          void* x_perm, hipStream_t stream);
 
+// One 16-byte piece per thread: groups of 16 rows of `row_bytes` bytes into
+// 1024-byte blocks (see MOE_LAYOUT_BLOCKED16).
+hipError_t launch_pack_blocked16(const void* src, void* dst, int64_t groups, int64_t row_bytes, hipStream_t stream);
+
 hipError_t launch_combine(int dtype, const void* y, const float* topk_w, const int32_t* row_of, int T,
                           int k, int d, void* out, hipStream_t stream);
 
@@ -77,6 +81,7 @@ struct GemmArgs {
   int E, K, N;
   int max_tiles;
   int skew_map;              // 1: uneven tile counts per expert deal chunks of units to the XCDs in turn
+  int blocked16;             // 1: weights in 16-row blocked order (moe_weight_layout_t)
 };
 
 hipError_t launch_gemm_bf16_gateup(int BM, const GemmArgs& a, hipStream_t stream);

@@ -57,6 +57,17 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
+/* Storage order of the expert weight matrices (w_gate, w_up [E][F][d] and
+ * w_down [E][d][F], bf16/fp32 values or E4M3 codes alike):
+ *  MOE_LAYOUT_ROWS:      row-major, K contiguous within each row;
+ *  MOE_LAYOUT_BLOCKED16: the rows of each matrix in groups of 16; a group is
+ *      stored as consecutive 1024-byte blocks, block c holding bytes
+ *      [64c, 64c + 64) of each of the group's 16 rows in row order.  Every
+ *      matrix keeps its byte range; only the order inside each 16-row group
+ *      changes.  The grouped GEMMs then read each wavefront's weights as
+ *      one contiguous stream.  moe_pack_blocked16 converts. */
+typedef enum moe_weight_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_BLOCKED16 = 1 } moe_weight_layout_t;
+
 /* Problem shape.  capacity = 0: uncapped dispatch; capacity = C >= 1:
  * capacity-bounded dispatch with an overflow pass. */
 typedef struct moe_shape {
@@ -70,6 +81,8 @@ typedef struct moe_shape {
   int32_t tile_rows;/* row-tile height of the grouped GEMMs: 0 lets the
                        library choose; else one of 16, 32, 48, 64, 96,
                        128, 160, 192 (others: MOE_ERR_UNSUPPORTED)      */
+  int32_t weight_layout; /* moe_weight_layout_t of the expert weights
+                       (the router weights are always row-major)        */
 } moe_shape_t;
 
 /* Sizes derived from a shape (all host values). */
@@ -209,6 +222,15 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
                          const int32_t* topk_ids_in, const float* topk_w_in, const void* w_gate,
                          const void* w_up, const void* w_down, void* out, void* workspace,
                          size_t ws_bytes, moe_forward_views_t* views_out, hipStream_t stream);
+
+/* Re-store `matrices` row-major matrices of `rows` rows of `row_bytes` bytes
+ * each (src, contiguous) in MOE_LAYOUT_BLOCKED16 order (dst, same size, must
+ * not overlap src; both 16-byte aligned).  A byte permutation: any element
+ * type.  rows must be a multiple of 16 and row_bytes of 64 (else
+ * MOE_ERR_INVALID_ARG).  Meant to run once when weights are loaded, not per
+ * layer call. */
+moe_status_t moe_pack_blocked16(const void* src, void* dst, int64_t matrices, int64_t rows, int64_t row_bytes,
+                                hipStream_t stream);
 
 /* ---- fp8 expert weights ------------------------------------------------
  * The TEMPO review (pith.science verdict for arXiv 2608.13057, referee

@@ -99,6 +99,24 @@ def widen_expert(w, e: int, dtype: str) -> np.ndarray:
     return to_f64(w[e], dtype)
 
 
+def blocked16(a: np.ndarray) -> np.ndarray:
+    """Reference of the library's blocked 16-row weight storage order.
+
+    Not a step of the layer: a byte order the GPU library accepts for its
+    expert weights.  For every matrix [rows, row_bytes] (rows % 16 == 0,
+    row_bytes % 64 == 0) the rows are taken in groups of 16 and each group is
+    written as consecutive 1024-byte blocks, block c holding bytes
+    [64c, 64c + 64) of the group's 16 rows in row order.  `a` is any array
+    whose last two axes are (rows, K); the result has the same shape and
+    dtype and holds the reordered bytes.
+    """
+    a = np.ascontiguousarray(a)
+    b = a.view(np.uint8).reshape(-1, a.shape[-2], a.shape[-1] * a.itemsize)
+    m, rows, rb = b.shape
+    out = b.reshape(m, rows // 16, 16, rb // 64, 64).transpose(0, 1, 3, 2, 4)
+    return np.ascontiguousarray(out).reshape(-1).view(a.dtype).reshape(a.shape)
+
+
 # ----------------------------------------------------------------------------
 # Step 1: routing
 # ----------------------------------------------------------------------------

@@ -41,8 +41,8 @@ def test_status_strings():
     assert b"unknown" in lib.moe_status_string(99)
 
 
-def _shape(T=64, d=128, E=8, k=2, F=256, C=0, dt=1, bm=0):
-    return MoeShape(T, d, E, k, F, C, dt, bm)
+def _shape(T=64, d=128, E=8, k=2, F=256, C=0, dt=1, bm=0, layout=0):
+    return MoeShape(T, d, E, k, F, C, dt, bm, layout)
 
 
 def _query(s):
@@ -173,6 +173,28 @@ def test_carve_and_workspace_checks():
 def test_views_struct_layout():
     # the Python mirror of moe_forward_views_t: a dispatch struct and 5 pointers
     assert ctypes.sizeof(MoeDispatch) == 10 * 8 + 8
-    assert ctypes.sizeof(MoeShape) == 8 * 4
+    assert ctypes.sizeof(MoeShape) == 9 * 4
     assert ctypes.sizeof(MoeForwardViews) == ctypes.sizeof(MoeDispatch) + 5 * 8
     assert ctypes.sizeof(MoeSizes) == 8 + 4 * 4 + 3 * 8
+
+
+def test_weight_layout_field_is_validated():
+    for layout, code in ((0, 0), (1, 0), (2, 1), (-1, 1)):
+        st, _ = _query(_shape(layout=layout))
+        assert st == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 4096, 1, 16, 64), 2),            # null src
+    ((4096, 0, 1, 16, 64), 2),            # null dst
+    ((4096, 1 << 20, 0, 16, 64), 1),      # no matrices
+    ((4096, 1 << 20, 1, 24, 64), 1),      # rows not a multiple of 16
+    ((4096, 1 << 20, 1, 16, 96), 1),      # row bytes not a multiple of 64
+    ((4096, 4096 + 512, 1, 16, 64), 1),   # dst overlaps src (1024 bytes each)
+    ((4104, 1 << 20, 1, 16, 64), 1),      # src not 16-byte aligned
+])
+def test_pack_blocked16_validation(args, code):
+    # validation returns before any HIP call, so fake addresses are safe here
+    lib = _lib.lib()
+    src, dst, m, rows, rb = args
+    assert lib.moe_pack_blocked16(src or None, dst or None, m, rows, rb, None) == code

@@ -481,3 +481,20 @@ def test_fp8_scale_is_per_output_channel():
     u = su[0].astype(np.float64) * sx
     hsum = float(np.sum(g / (1 + np.exp(-g)) * u))
     np.testing.assert_allclose(r["out"][0], sd[0].astype(np.float64) * hsum, rtol=1e-13)
+
+
+def test_blocked16_layout_by_hand():
+    # 2 matrices of 32 rows x 128 bytes: byte (m, r, b) must land at
+    # m*4096 + (r // 16)*2048 + (b // 64)*1024 + (r % 16)*64 + b % 64
+    rng = np.random.default_rng(4)
+    a = rng.integers(0, 256, size=(2, 32, 128), dtype=np.uint8)
+    out = O.blocked16(a).reshape(-1)
+    for m in range(2):
+        for r in range(32):
+            for b in range(0, 128, 7):
+                pos = m * 4096 + (r // 16) * 2048 + (b // 64) * 1024 + (r % 16) * 64 + b % 64
+                assert out[pos] == a[m, r, b]
+    # a permutation of bytes; element types keep their bytes together
+    assert sorted(out.tolist()) == sorted(a.reshape(-1).tolist())
+    w = rng.standard_normal((3, 16, 64)).astype(np.float32)
+    assert sorted(O.blocked16(w).reshape(-1).tolist()) == sorted(w.reshape(-1).tolist())
