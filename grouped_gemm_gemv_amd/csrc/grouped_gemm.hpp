@@ -26,15 +26,20 @@
 // splitting N alone would not give enough workgroups to fill the GPU).
 //
 // Data movement per iteration (WK steps):
-//  - the activation tile (MS*16 rows x WK*128 bytes) is loaded by the whole
-//    workgroup two iterations ahead into registers and written, one
-//    iteration ahead, into a double-buffered LDS tile (rows padded by 16 bytes so 16-byte lane reads
-//    of 16 consecutive rows hit distinct banks); rows past the tile's last
-//    row read as zeros;
+//  - the activation tile (MS*16 rows x WK*128 bytes) goes through a ring of
+//    PF+1 LDS stages, PF iterations ahead, written by LDS-direct buffer loads
+//    (no register round trip); with the gather folded in, each row's source
+//    is row token_of[r] of x.  Chunk c of row r sits at c ^ (r & 7) so the
+//    MFMA operand reads are free of bank conflicts; rows past the tile's
+//    last row read as zeros;
 //  - weights are streamed by each wavefront straight into MFMA operand
 //    registers, PF iterations ahead, with no LDS round trip: no weight byte
 //    is shared between wavefronts, and every weight byte is read from HBM
-//    once per row tile.
+//    once per row tile.  In the blocked 16-row storage order a wavefront's
+//    weights are one contiguous stream; row-major weights are read with a
+//    row stride.  E4M3 weights (WQ) load 16 codes per lane per step and are
+//    widened to bf16 in registers; their channel scales multiply the fp32
+//    sums in the epilogue.
 // Loads are buffer loads: one descriptor per operand (bounded by the tile's
 // rows, or by N for a column tail) plus 32-bit lane offsets, and reads past
 // the bound return zero.  Every iteration issues the same loads (past the

@@ -25,7 +25,8 @@
  *    validation error nothing is enqueued and no HIP call is made.  After
  *    enqueueing, a launch failure reported by hipGetLastError is returned as
  *    MOE_ERR_HIP.
- *  - Matrices are row-major.  x, the router and expert weights, the permuted
+ *  - Matrices are row-major (expert weights may instead be stored in the
+ *    blocked 16-row order, see moe_weight_layout_t).  x, the router and expert weights, the permuted
  *    activations, the SwiGLU intermediate, the expert outputs and the layer
  *    output all have the element type `dtype` (fp32 or bf16); routing weights
  *    are always fp32 and indices int32.  Accumulation is fp32.
@@ -205,7 +206,7 @@ moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm, const float* 
  * pointers; valid until the workspace is reused). */
 typedef struct moe_forward_views {
   moe_dispatch_t disp;  /* dispatch arrays                                     */
-  int32_t* topk_ids;    /* [T,k] routing used (computed, or a copy of the input) */
+  int32_t* topk_ids;    /* [T,k] routing used (computed here, or topk_ids_in) */
   float* topk_w;        /* [T,k]                                               */
   void* x_perm;         /* NULL: moe_forward does not materialise x_perm; its
                            gate+up GEMM reads row token_of[r] of x directly  */
