@@ -9,7 +9,7 @@ namespace moe {
 // Entries handled by one block of the counting and scatter kernels.
 constexpr int kCountChunk = 2048;
 // Tokens per block of the router kernel.
-constexpr int kRouteTokens = 16;
+constexpr int kRouteSmallBatch = 2048;  // below: 4 tokens per router workgroup, else 16
 
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* bias, int T, int d,
                         int E, int k, int32_t* topk_ids, float* topk_w, hipStream_t stream);
