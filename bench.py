@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first copy 256 MiB device to device 3 times (reference for PMC byte counters)")
     ap.add_argument("--summarize", metavar="DB", help="print a text summary of a rocprofv3 result database and exit")
+    ap.add_argument("--kernel-table", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "TRACE_DB"),
+                    help="per kernel: HBM bytes per dispatch from a FETCH_SIZE and a WRITE_SIZE run (both with "
+                         "--pmc-calibration), mean duration from a kernel trace, achieved GB/s; then exit")
     ap.add_argument("--cost-curve", action="store_true",
                     help="per-expert cost curve: time the grouped GEMMs with every expert given n rows, "
                          "for n from 1 to 1024, fit t = max(a, c + b*n) and exit")
@@ -105,11 +108,14 @@ def summarize(db_path: str):
     db = sqlite3.connect(db_path)
     views = {r[0] for r in db.execute("select name from sqlite_master where type in ('view','table')")}
     if "pmc_events" in views and db.execute("select count(*) from pmc_events").fetchone()[0]:
-        rows = db.execute("select name, counter_name, counter_value from pmc_events").fetchall()
+        rows = db.execute("select name, dispatch_id, counter_name, counter_value from pmc_events").fetchall()
+        per = collections.defaultdict(float)  # a counter may come as several rows (one per SE) per dispatch
+        for name, did, cn, cv in rows:
+            per[(name, cn, did)] += cv
         acc = collections.defaultdict(list)
-        for name, cn, cv in rows:
-            acc[(name, cn)].append(cv)
-        print(f"# PMC summary of {os.path.basename(db_path)}: kernel | counter | dispatches | mean value")
+        for (name, cn, _), v in per.items():
+            acc[(name, cn)].append(v)
+        print(f"# PMC summary of {os.path.basename(db_path)}: kernel | counter | dispatches | mean value per dispatch")
         for (name, cn), vals in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
             print(f"{name[:110]} | {cn} | {len(vals)} | {sum(vals) / len(vals):.1f}")
     else:
@@ -161,6 +167,39 @@ def pmc_summary(fetch_db: str, write_db: str, workload: str):
         f, _ = out[(key, "FETCH_SIZE")]
         w, _ = out[(key, "WRITE_SIZE")]
         print(f"{key}_hbm_bytes_per_launch: {round((f * sf + w * sw) * 1024)}")
+
+
+def kernel_table(fetch_db: str, write_db: str, trace_db: str):
+    """Achieved HBM bandwidth of every kernel: counter bytes per dispatch
+    (scaled by the calibration copies, as in pmc_summary) over the mean
+    duration of the same kernel in a kernel-trace run of the same command."""
+    import collections
+    import sqlite3
+
+    def counter(db_path, name):
+        db = sqlite3.connect(db_path)
+        rows = db.execute("select name, dispatch_id, counter_value from pmc_events where counter_name = ? "
+                          "order by dispatch_id", (name,)).fetchall()
+        copies = [v for n, _, v in rows if "copyBuffer" in n][:3]
+        scale = (256 * 1024 * 1024 / 1024) / (sum(copies) / 3)
+        acc = collections.defaultdict(list)
+        for n, _, v in rows[3:] if len(copies) == 3 else rows:
+            acc[n].append(v * scale * 1024)
+        return {n: sum(v) / len(v) for n, v in acc.items()}
+
+    fetch = counter(fetch_db, "FETCH_SIZE")
+    write = counter(write_db, "WRITE_SIZE")
+    db = sqlite3.connect(trace_db)
+    dur = collections.defaultdict(list)
+    for n, d in db.execute("select name, end - start from kernels"):
+        dur[n].append(d)
+    print("# kernel | HBM read MB | HBM write MB | mean us (trace) | GB/s")
+    for n in sorted(fetch, key=lambda k: -(fetch[k] + write.get(k, 0))):
+        if n not in dur or "copyBuffer" in n:
+            continue
+        d = sorted(dur[n])[len(dur[n]) // 2] / 1000  # median us
+        rd, wr = fetch[n] / 1e6, write.get(n, 0) / 1e6
+        print(f"{n[:100]} | {rd:.2f} | {wr:.2f} | {d:.2f} | {(rd + wr) * 1e3 / d:.0f}")
 
 
 def fit_knee(n, t):
@@ -319,6 +358,9 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload)
+        return
+    if args.kernel_table:
+        kernel_table(*args.kernel_table)
         return
     if args.cost_curve:
         if args.gpus != 1:
