@@ -303,21 +303,23 @@ def cost_curve(args):
     print(json.dumps(summary), flush=True)
 
 
-def gemm_work(wl, counts, dt_bytes):
-    """Algorithmic FLOPs and HBM bytes of the two grouped GEMMs (per launch):
-    every active expert's weights once (E4M3 codes: 1 byte per element plus
-    one fp32 scale per output channel), activation rows read once per slot,
-    outputs written once."""
+def gemm_work(wl, counts, dt_bytes, spill_counts=None):
+    """Algorithmic FLOPs and HBM bytes of the two grouped GEMMs (all passes):
+    every active expert's weights once, plus once more for every expert with
+    rows in the overflow pass (capacity mode; that re-streaming is the method's
+    own cost), E4M3 codes at 1 byte per element plus one fp32 scale per output
+    channel; activation rows read once per slot, outputs written once."""
     Tk = wl.T * wl.k
     active = int((counts > 0).sum())
+    streams = active + (int((spill_counts > 0).sum()) if spill_counts is not None else 0)
     gu_flops = 4.0 * Tk * wl.d * wl.F
     dn_flops = 2.0 * Tk * wl.d * wl.F
     if wl.weights == "e4m3":
-        wgu = active * (2.0 * wl.F * wl.d + 2.0 * wl.F * 4)
-        wdn = active * (1.0 * wl.F * wl.d + wl.d * 4)
+        wgu = streams * (2.0 * wl.F * wl.d + 2.0 * wl.F * 4)
+        wdn = streams * (1.0 * wl.F * wl.d + wl.d * 4)
     else:
-        wgu = active * 2.0 * wl.F * wl.d * dt_bytes
-        wdn = active * 1.0 * wl.F * wl.d * dt_bytes
+        wgu = streams * 2.0 * wl.F * wl.d * dt_bytes
+        wdn = streams * 1.0 * wl.F * wl.d * dt_bytes
     gu_bytes = wgu + (Tk * wl.d + Tk * wl.F) * dt_bytes
     dn_bytes = wdn + (Tk * wl.F + Tk * wl.d) * dt_bytes
     return gu_flops, gu_bytes, dn_flops, dn_bytes, active
@@ -426,6 +428,7 @@ def main():
     views = step()
     torch.cuda.synchronize()
     counts = views.disp.arrays()["counts"].cpu().numpy()
+    spill_counts = views.disp.arrays()["spill_counts"].cpu().numpy() if wl.capacity else None
     log(f"eager forward ok; tile rows {q.tile_rows}, counts {counts.tolist()[:16]}")
 
     # graph capture of the whole layer (no host sync, no allocation inside)
@@ -508,7 +511,7 @@ def main():
               "p90": round(float(np.percentile(per, 90)), 4)}
 
 
-    gu_flops, gu_bytes, dn_flops, dn_bytes, active = gemm_work(wl, counts, dt_bytes)
+    gu_flops, gu_bytes, dn_flops, dn_bytes, active = gemm_work(wl, counts, dt_bytes, spill_counts)
     peak_f = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
     if gu_flops / gu_bytes < ridge:
