@@ -372,7 +372,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested); "
-              "the layer is not sharded across GPUs in this build.", file=sys.stderr)
+              "the layer runs on one GPU; it is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -342,7 +342,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: a shape field or size is out of range";
     case MOE_ERR_NULL_PTR: return "MOE_ERR_NULL_PTR: a required pointer is NULL";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace below the queried size";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid arguments this build does not implement";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid arguments the library does not implement";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
     default: return "unknown moe_status_t";
   }
