@@ -327,7 +327,7 @@ def gemm_work(wl, counts, dt_bytes, spill_counts=None):
 
 def cpu_baseline(wl, inp, sample_tokens):
     """The oracle as it stands on the workload (or its first `sample_tokens`
-    tokens), repeated until about 10 s of CPU time have been spent."""
+    tokens), repeated until about 12 s of CPU time have been spent."""
     from threadpoolctl import threadpool_limits
 
     from oracle import moe_oracle as O
@@ -338,7 +338,7 @@ def cpu_baseline(wl, inp, sample_tokens):
     cores = min(16, os.cpu_count() or 1)
     reps, total = 0, 0.0
     with threadpool_limits(limits=cores):
-        while reps == 0 or (total < 10.0 and reps < 5):
+        while reps == 0 or (total < 12.0 and reps < 10):
             t0 = time.perf_counter()
             if inp.topk_ids is None:
                 O.forward(inp.x[:n], inp.wr, wg, wu, wd, wl.k, wl.dtype, bias=inp.bias,
