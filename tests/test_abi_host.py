@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from grouped_gemm_gemv_amd import _lib
@@ -198,3 +199,37 @@ def test_pack_blocked16_validation(args, code):
     lib = _lib.lib()
     src, dst, m, rows, rb = args
     assert lib.moe_pack_blocked16(src or None, dst or None, m, rows, rb, None) == code
+
+
+def test_query_random_and_extreme_shapes():
+    """moe_query on random and extreme shapes: either a clean validation error
+    or sizes that agree with the definitions (no overflow, no crash)."""
+    rng = np.random.default_rng(77)
+    shapes = []
+    for _ in range(400):
+        E = int(rng.integers(1, 257))
+        shapes.append(dict(T=int(rng.choice([1, 7, 512, 4096, 1 << 16, 1 << 20, (1 << 31) - 1])),
+                           d=int(64 * rng.integers(1, 256)), E=E, k=int(rng.integers(1, min(E, 64) + 1)),
+                           F=int(64 * rng.integers(1, 512)),
+                           C=int(rng.choice([0, 1, 384, 1 << 20, (1 << 31) - 1])),
+                           bm=int(rng.choice([0, 0, 16, 192]))))
+    shapes += [dict(T=1, d=64, E=256, k=64, F=64, C=0, bm=0),
+               dict(T=(1 << 31) - 1, d=64, E=256, k=64, F=64, C=0, bm=0),
+               dict(T=1 << 24, d=64, E=256, k=64, F=64, C=(1 << 31) - 1, bm=0)]
+    ok = 0
+    for sh in shapes:
+        st, q = _query(_shape(T=sh["T"], d=sh["d"], E=sh["E"], k=sh["k"], F=sh["F"], C=sh["C"], bm=sh["bm"]))
+        assert st in (0, 1), (sh, st)
+        if st != 0:
+            # errors only where a count or index would not fit in int32
+            Tk = sh["T"] * sh["k"]
+            R = O.row_space(sh["T"], sh["k"], sh["E"], sh["C"])
+            assert Tk >= 2 ** 31 - 1 or R >= 2 ** 31 - 1 or sh["E"] * sh["C"] >= 2 ** 31 - 1, sh
+            continue
+        ok += 1
+        assert q.rows == O.row_space(sh["T"], sh["k"], sh["E"], sh["C"])
+        for p in (0, 1):
+            assert q.max_tiles >= O.max_tiles(sh["T"], sh["k"], sh["E"], sh["C"], q.tile_rows, p)
+        assert q.forward_ws_bytes >= q.rows * (sh["d"] + sh["F"]) * 2 + q.dispatch_bytes
+        assert q.forward_ws_bytes < 2 ** 62
+    assert ok > 100
