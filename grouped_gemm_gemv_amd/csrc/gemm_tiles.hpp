@@ -24,8 +24,8 @@ struct TileCfg;
 // evens out the last wave of units (decode T = 1: 148 vs 154 us per layer).
 template <> struct TileCfg<16, true> { using type = TileShape<16, 16, 1, 4, 4>; };
 template <> struct TileCfg<32, true> { using type = TileShape<32, 32, 1, 4, 4>; };
-template <> struct TileCfg<48, true> { using type = TileShape<48, 32, 2, 2, 4>; };
-template <> struct TileCfg<64, true> { using type = TileShape<64, 32, 2, 2, 4>; };
+template <> struct TileCfg<48, true> { using type = TileShape<48, 16, 4, 2, 4>; };
+template <> struct TileCfg<64, true> { using type = TileShape<64, 16, 4, 2, 4>; };
 template <> struct TileCfg<96, true> { using type = TileShape<96, 16, 8, 1, 4>; };
 template <> struct TileCfg<128, true> { using type = TileShape<128, 16, 8, 1, 4>; };
 template <> struct TileCfg<160, true> { using type = TileShape<160, 16, 7, 1, 4>; };
@@ -34,8 +34,8 @@ template <> struct TileCfg<192, true> { using type = TileShape<192, 16, 8, 1, 4>
 // down projection
 template <> struct TileCfg<16, false> { using type = TileShape<16, 16, 1, 4, 4>; };
 template <> struct TileCfg<32, false> { using type = TileShape<32, 32, 1, 4, 4>; };
-template <> struct TileCfg<48, false> { using type = TileShape<48, 32, 2, 2, 4>; };
-template <> struct TileCfg<64, false> { using type = TileShape<64, 32, 2, 2, 4>; };
+template <> struct TileCfg<48, false> { using type = TileShape<48, 16, 4, 2, 4>; };
+template <> struct TileCfg<64, false> { using type = TileShape<64, 16, 4, 2, 4>; };
 template <> struct TileCfg<96, false> { using type = TileShape<96, 16, 8, 1, 4>; };
 template <> struct TileCfg<128, false> { using type = TileShape<128, 16, 8, 1, 4>; };
 template <> struct TileCfg<160, false> { using type = TileShape<160, 16, 8, 1, 4>; };
