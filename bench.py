@@ -244,15 +244,20 @@ def cost_curve(args):
     wg = (torch.randn((Eg, wl.F, wl.d), device="cuda", generator=g) * 0.02).to(dt)
     wu = (torch.randn((Eg, wl.F, wl.d), device="cuda", generator=g) * 0.02).to(dt)
     wd = (torch.randn((Eg, wl.d, wl.F), device="cuda", generator=g) * 0.02).to(dt)
+    blocked = args.weight_layout == "blocked16"
+    if blocked:
+        wg, wu, wd = M.moe_pack_blocked16(wg), M.moe_pack_blocked16(wu), M.moe_pack_blocked16(wd)
     cur = torch.cuda.current_stream()
     rows = [1, 2, 4, 8, 16, 24, 32, 48, 64, 80, 96, 128, 160, 192, 224, 256, 320, 384, 448, 512, 640, 768, 1024]
     res = []
-    print(f"# per-expert cost curve: {Eg} experts x n rows, d={wl.d}, F={wl.F}, {wl.dtype}; "
-          f"one gate+up and one down launch, HIP events, median of 5 runs of {args.kernel_iters} calls")
+    print(f"# per-expert cost curve: {Eg} experts x n rows, d={wl.d}, F={wl.F}, {wl.dtype}, "
+          f"{args.weight_layout} weights; one gate+up and one down launch, HIP events, median of 5 runs of "
+          f"{args.kernel_iters} calls")
     print("# n | tile rows | gate+up us | down us | total us | us per expert | TFLOP/s | weight TB/s")
     for n in rows:
         T = n * Eg
-        shape = M.Shape(T, wl.d, Eg, 1, wl.F, 0, dt, args.cost_tile_rows)
+        shape = M.Shape(T, wl.d, Eg, 1, wl.F, 0, dt, args.cost_tile_rows,
+                        M.LAYOUT_BLOCKED16 if blocked else M.LAYOUT_ROWS)
         q = M.query(shape)
         x = (torch.randn((T, wl.d), device="cuda", generator=g)).to(dt)
         ids = (torch.arange(T, device="cuda", dtype=torch.int32) // n).reshape(T, 1).contiguous()

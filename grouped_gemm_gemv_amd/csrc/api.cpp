@@ -49,9 +49,24 @@ int choose_tile_rows(const moe_shape_t& s) {
   const int64_t active = std::min<int64_t>(s.E, Tk);
   int64_t mean = ceil_div(Tk, active);
   if (s.capacity > 0) mean = std::min<int64_t>(mean, s.capacity);
+  // A token or two per expert: 16-row split-K tiles stream the weights best.
+  if (mean <= 2) return 16;
+  // Tall tiles once enough of them exist to fill the units; a lone expert stays
+  // on 64-row split-K tiles up to 512 rows (one Mixtral expert: 64 rows 143 us,
+  // 160 rows 197 us at 256 rows).
   const int64_t tall_tiles = active * ceil_div(s.d, 128);
-  if (tall_tiles >= kComputeUnits * 3 / 4 || (mean > 64 && tall_tiles >= 64) || mean > 128)
-    return (mean <= 160 && s.F % 112 == 0) ? 160 : 192;
+  if (tall_tiles >= kComputeUnits * 3 / 4 || (mean > 64 && tall_tiles >= 64) || mean > 512) {
+    // 192 rows (256-column down tiles) once there are many such tiles; past 160
+    // rows also with fewer, unless 160-row tiles pad less below 320 rows.  On
+    // 8 experts of d = 3584: 64 rows 85 us at 160 vs 91 at 192, 192 rows 193 vs
+    // 155 us; 8 Mixtral experts of 192 rows: 1001 vs 748 us; 32 or more
+    // experts of d = 3584: 192 ahead by 2-7 %.
+    const int64_t r192 = ceil_div(mean, 192);
+    const int64_t w192 = active * r192 * ceil_div(s.d, 256);
+    const bool past160 = w192 >= 112 && mean > 160 &&
+                         (mean > 320 || r192 * 192 <= ceil_div(mean, 160) * 160);
+    return (w192 >= 448 || past160) ? 192 : 160;
+  }
   if (mean > 32) return 64;
   if (active * ceil_div(s.d, 64) >= kComputeUnits) return 48;
   return (mean * 5 + 3) / 4 <= 16 ? 16 : 32;

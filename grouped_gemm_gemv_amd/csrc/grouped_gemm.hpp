@@ -100,7 +100,7 @@ __device__ __forceinline__ uint4 widen_e4m3(unsigned lo, unsigned hi) {
 
 // WQ: the weights are OCP E4M3 codes with one fp32 scale per output channel
 // (weight row); the activations stay bf16.
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int WAUX, bool WQ>
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ>
 struct Gemm {
   using Elt = typename Tr::T;
   static_assert(!WQ || std::is_same<Tr, TBF16>::value, "fp8 weights take bf16 activations");
@@ -148,7 +148,12 @@ struct Gemm {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
   }
 
-  template <int MS>
+  // Cache policy of the weight loads: kNonTemporal streams them past the
+  // caches' normal replacement order.  Used only where no other workgroup
+  // reads the same weights (see run_ms).
+  static constexpr int kNonTemporal = 2;
+
+  template <int MS, int WAUX>
   __device__ __forceinline__ static void run(const Ctx& c) {
     // The activation tile of an iteration (MS*16 rows x ROWB bytes) is moved
     // by LDS-direct buffer loads: one wavefront instruction fills 1 KB of LDS
@@ -373,21 +378,30 @@ struct Gemm {
     }
   }
 
+  // Main loop for exactly ms subtiles.  `once`: the expert has a single row
+  // tile in this launch, so each weight byte is read by one workgroup only;
+  // tiles of at most NTMS subtiles then load the weights non-temporally.
   template <int M>
-  __device__ __forceinline__ static void run_ms(int ms, const Ctx& c) {
+  __device__ __forceinline__ static void run_ms(int ms, bool once, const Ctx& c) {
     if constexpr (M >= 1) {
       if (ms == M) {
-        run<M>(c);
+        if constexpr (M <= NTMS) {
+          if (once) {
+            run<M, kNonTemporal>(c);
+            return;
+          }
+        }
+        run<M, 0>(c);
         return;
       }
-      run_ms<M - 1>(ms, c);
+      run_ms<M - 1>(ms, once, c);
     }
   }
 };
 
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int WAUX, bool WQ>
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ>
 __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) {
-  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, WAUX, WQ>;
+  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, NTMS, WQ>;
   // one LDS array per activation stage (stages past NA are 16-byte stubs)
   __shared__ __attribute__((aligned(16))) char st0[G::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[G::STAGE];
@@ -494,7 +508,7 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
     c.scale[0] = p.s0 + (size_t)e * p.N;
     c.scale[G::NMAT - 1] = (GATED ? p.s1 : p.s0) + (size_t)e * p.N;
   }
-  G::template run_ms<G::MSUB>((ent.z + 15) >> 4, c);
+  G::template run_ms<G::MSUB>((ent.z + 15) >> 4, mt == 1, c);
 }
 
 template <class Tr, class Cfg, bool GATED, bool WQ>
@@ -505,7 +519,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const long long round = a.skew_map ? 8LL * kXcdChunk : 8;  // chunked mapping: whole rounds of chunks
   const long long grid = ((units + round - 1) / round) * round;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::WAUX, WQ>),
+  hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::NTMS, WQ>),
                      dim3((unsigned)grid), dim3(64 * Cfg::WN * Cfg::WK), 0, stream, a);
   return hipGetLastError();
 }

@@ -76,13 +76,13 @@ def test_tile_rows_override():
 
 
 @pytest.mark.parametrize("name,bm", [
-    ("mixtral_t512", 160),        # 8 experts x 32 down column tiles fill the 256 compute units; 112 | F
-    ("mixtral_t4096", 192),       # mean 1024 rows: the tallest tile
+    ("mixtral_t512", 160),        # 8 experts x 32 down column tiles fill the units; 128 rows pad less at 160
+    ("mixtral_t4096", 192),       # 8 x 6 x 16 = 768 tiles of 192 rows: the tallest tile
     ("mixtral_decode_t1", 16),    # 2 active experts: split-K short tiles keep the units up
-    ("mixtral_decode_t8", 160),   # min(E, T*k) = 8 experts can be active
-    ("mixtral_decode_t128", 160),
-    ("e64_zipf_a2.0", 192),       # 112 does not divide F = 2560
-    ("capacity_gini0.10", 192),
+    ("mixtral_decode_t8", 16),    # two rows per active expert: 16-row split-K tiles
+    ("mixtral_decode_t128", 160), # 8 experts x 32 tall down tiles fill the units
+    ("e64_zipf_a2.0", 192),       # 64 experts x 14 256-column down tiles
+    ("capacity_gini0.10", 192),   # 384 rows: 2 tiles of 192, 64 x 2 x 8 of them
     ("tiny_f32", 32),             # one 128-column down tile per expert: mean 16 -> 1.25x -> 32
 ])
 def test_automatic_tile_rows(name, bm):
@@ -95,10 +95,15 @@ def test_automatic_tile_rows(name, bm):
     (16, 1, 1, 4096, 14336, 32),    # one expert, 16 rows: split-K 32-row tiles
     (64, 1, 1, 4096, 14336, 64),    # past 32 rows: 64-row split-K tiles
     (128, 1, 1, 4096, 14336, 64),   # 32 tall down tiles only: stay short
-    (256, 1, 1, 4096, 14336, 192),  # past 128 rows: tall
+    (256, 1, 1, 4096, 14336, 64),   # a lone expert stays short up to 512 rows
+    (1024, 1, 1, 4096, 14336, 160), # past 512 rows: tall, too few tiles for 192
     (256, 2, 1, 4096, 14336, 160),  # 128 rows, 64 tall down tiles: tall
     (128, 8, 1, 2048, 1408, 48),    # 16 rows, 8 x 32 64-column tiles fill the chip
-    (256, 8, 2, 3584, 2560, 192),   # 224 tall down tiles >= 192
+    (256, 8, 2, 3584, 2560, 160),   # 224 tall down tiles >= 192; 8 x 14 tiles of 192 rows too few
+    (1024, 32, 2, 3584, 2560, 192), # 32 x 14 = 448 tiles of 192 rows
+    (1536, 8, 1, 3584, 2560, 192),  # 192 rows: one 192-row tile beats 160 + 32
+    (2048, 8, 1, 2048, 1408, 160),  # 256 rows: 2 x 160 pads less than 2 x 192
+    (3584, 8, 1, 2048, 1408, 192),  # 448 rows, 8 x 3 x 8 tiles of 192 rows
 ])
 def test_tile_rows_rule_shapes(T, E, k, d, F, bm):
     st, q = _query(_shape(T=T, d=d, E=E, k=k, F=F))
