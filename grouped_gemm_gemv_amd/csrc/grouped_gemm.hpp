@@ -267,9 +267,9 @@ struct Gemm {
     // The gate+up kernel raises the wavefront's issue priority while it issues
     // loads, so a wavefront busy with MFMAs on the same SIMD does not delay the
     // next loads (measured 1.5 % at 128 rows per expert; no gain for down).
-    auto body = [&](int it, auto uc) {
+    auto body = [&](int it, auto uc, auto waitc) {
       constexpr int u = decltype(uc)::value;
-      wait_vm<WAITN>();
+      wait_vm<decltype(waitc)::value>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       if constexpr (GATED) __builtin_amdgcn_s_setprio(2);
@@ -290,10 +290,18 @@ struct Gemm {
     }
     int it0 = 0;
     for (; it0 + NA <= c.nit; it0 += NA) {
-      static_for<NA>([&](auto uc) { body(it0 + decltype(uc)::value, uc); });
+      static_for<NA>([&](auto uc) { body(it0 + decltype(uc)::value, uc, std::integral_constant<int, WAITN>{}); });
     }
+    // The last nit mod NA iterations.  Their weight loads fetch values no
+    // later iteration uses, and the compiler may drop them, so tail
+    // iteration u counts only what is surely issued after its own loads: the
+    // loop's last PF - 1 - u iterations, and the activation loads of the u
+    // tail iterations before it.  (Waiting for WAITN there could let a
+    // wavefront reach the barrier before its activation loads had landed.)
     static_for<NA>([&](auto uc) {
-      if (it0 + decltype(uc)::value < c.nit) body(it0 + decltype(uc)::value, uc);
+      constexpr int u = decltype(uc)::value;
+      constexpr int n = u < PF ? (PF - 1 - u) * (QW + WL) + u * QW : 0;
+      if (it0 + u < c.nit) body(it0 + u, uc, std::integral_constant<int, n>{});
     });
     // the trailing (clamped) loads still write LDS: drain them before the
     // LDS is reused or the wavefront ends
