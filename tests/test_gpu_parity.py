@@ -50,6 +50,12 @@ CASES = {
     "bf16_cap_c1": ("capacity_gini0.30", dict(T=100, d=64, E=8, k=2, F=64, capacity=1)),
     "bf16_one_expert": ("e64_zipf_a2.0", dict(T=300, d=128, E=16, k=1, F=128, zipf_alpha=60.0)),
     "bf16_e256_k64": ("mixtral_t512", dict(T=33, d=64, E=256, k=64, F=64)),
+    # decode batches: one router workgroup and the one-block dispatch, at the
+    # sizes of each router tile (E <= 16, 32, 64), and the first T past 16
+    "bf16_t8": ("mixtral_t512", dict(T=8, d=256, F=128)),
+    "bf16_t16_e64": ("mixtral_t512", dict(T=16, d=256, E=64, k=6, F=128)),
+    "f32_t16_e32": ("tiny_f32", dict(T=16, E=32, k=4)),
+    "bf16_t17": ("mixtral_t512", dict(T=17, d=128, F=64)),
 }
 
 
@@ -213,6 +219,16 @@ def test_forward_matches_steps_and_is_deterministic(runs, case):
     assert np.array_equal(outs[0], outs[1])
     assert np.array_equal(outs[0], bits(r.out))
     assert np.array_equal(v.topk_ids.cpu().numpy(), r.gpu_ids)
+    assert np.array_equal(bits(v.topk_w), bits(r.w))
+    # the dispatch the layer built is the one moe_permute builds, array by
+    # array (tile map entries past n_tiles are unused)
+    fa, sa = v.disp.arrays(), r.disp.arrays()
+    for name in ("counts", "offsets", "spill_counts", "spill_offsets", "row_of", "token_of", "tile_off",
+                 "n_tiles", "err_flags"):
+        assert torch.equal(fa[name].cpu(), sa[name].cpu()), name
+    nt = sa["n_tiles"].cpu().numpy()
+    for p in range(2):
+        assert torch.equal(fa["tile_map"][p, :nt[p]].cpu(), sa["tile_map"][p, :nt[p]].cpu()), p
 
 
 @pytest.mark.parametrize("case", ["bf16_capacity", "f32_capacity"])
