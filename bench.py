@@ -72,12 +72,16 @@ def pmc_summary_path(workload: str) -> str:
 
 
 def gemm_source_hash() -> str:
-    """Hash of the grouped-GEMM sources: PMC traffic figures are only valid for this code."""
+    """Hash of the grouped-GEMM sources, comments and blank lines left out: PMC
+    traffic figures are only valid for this code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "grouped_gemm_gemv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "grouped_gemm_gemv_amd", "csrc", f), encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        code = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+        h.update("\n".join(line for line in code if line.strip()).encode())
     return h.hexdigest()[:16]
 
 

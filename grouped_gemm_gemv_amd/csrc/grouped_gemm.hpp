@@ -39,7 +39,9 @@
 //    weights are one contiguous stream; row-major weights are read with a
 //    row stride.  E4M3 weights (WQ) load 16 codes per lane per step and are
 //    widened to bf16 in registers; their channel scales multiply the fp32
-//    sums in the epilogue.
+//    sums in the epilogue.  When the expert has a single row tile (so no
+//    other workgroup reads these weights) and the tile has at most NTMS
+//    subtiles, the weight loads carry the non-temporal cache policy.
 // Loads are buffer loads: one descriptor per operand (bounded by the tile's
 // rows, or by N for a column tail) plus 32-bit lane offsets, and reads past
 // the bound return zero.  Every iteration issues the same loads (past the
