@@ -20,21 +20,17 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Largest row-tile height of the grouped GEMMs.  A tile holds up to BM rows
 // and only its non-empty 16-row subtiles are computed, so a tall tile costs
 // nothing for short experts.  The configurations come in two families:
-//  * tall (BM 160/192: 112- or 128-column workgroups, K not split) stream
+//  * tall (BM 160/192/384: 112- to 256-column workgroups, K not split) stream
 //    weights best and give a hot expert the fewest row tiles, but need many
 //    column tiles to occupy the 256 compute units;
 //  * short (BM 16/32: 32 columns, K split over 4 wavefronts; BM 48/64: 64
 //    columns, K split over 2) multiply the workgroups without duplicating a
 //    weight stream, for few active experts.
-// Measured rule (per-expert cost curves at the Mixtral and 64-expert shapes):
-// tall when the down projection has at least 192 tiles of 128 columns over
-// the experts that can be active, or when experts average more than 64 rows
-// and there are at least 64 such tiles; otherwise 64 rows for experts past 32
-// rows, 48 when 64-column tiles alone fill the chip, else the smallest of
-// 16/32 holding 1.25x the mean.  BM 160 is the 112-column gate+up tile, used
-// when 112 divides F and the mean expert fits in it.  The mean is T*k over
-// min(E, T*k) experts, at most C in the capacity pass.
-constexpr int kTileRows[] = {16, 32, 48, 64, 96, 128, 160, 192};
+// The rule below was fitted to per-expert cost curves measured on this GPU
+// (Mixtral, 64-expert and capacity shapes, blocked weights); each branch
+// states the measurement behind it.  The mean is T*k over min(E, T*k)
+// experts, at most C in the capacity pass.
+constexpr int kTileRows[] = {16, 32, 48, 64, 96, 128, 160, 192, 384};
 constexpr int kComputeUnits = 256;
 
 bool supported_tile_rows(int bm) {
@@ -65,7 +61,15 @@ int choose_tile_rows(const moe_shape_t& s) {
     const int64_t w192 = active * r192 * ceil_div(s.d, 256);
     const bool past160 = w192 >= 112 && mean > 160 &&
                          (mean > 320 || r192 * 192 <= ceil_div(mean, 160) * 160);
-    return (w192 >= 448 || past160) ? 192 : 160;
+    if (!(w192 >= 448 || past160)) return 160;
+    // A thousand rows or more per expert: 384-row tiles, which gate+up works
+    // in 128-row pieces with 32 weight rows per wavefront (twice the MFMAs
+    // per activation fragment read from LDS) and down in 192-row pieces.
+    // Mixtral, 8 experts of 1024 rows: 2590 vs 2826 us; with fewer rows the
+    // gain is uneven (8 experts of d = 2048 at 768 rows: 149 vs 139 us), and
+    // experts shorter than a tile leave pieces empty, whose workgroups still
+    // hold a compute unit while they find that out.
+    return mean >= 1024 ? 384 : 192;
   }
   if (mean > 32) return 64;
   if (active * ceil_div(s.d, 64) >= kComputeUnits) return 48;

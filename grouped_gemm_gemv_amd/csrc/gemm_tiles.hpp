@@ -18,9 +18,13 @@
 
 namespace moe {
 
-template <int BM_, int WTN_, int WN_, int WK_, int PF_, int NTMS_ = 0>
+template <int BM_, int WTN_, int WN_, int WK_, int PF_, int NTMS_ = 0, int RS_ = 1>
 struct TileShape {
   static constexpr int BM = BM_, WTN = WTN_, WN = WN_, WK = WK_, PF = PF_;
+  // A workgroup computes BM rows; a tile of the tile map (RS * BM rows) is
+  // split into RS such pieces, so the two GEMMs can work the same tile map
+  // in pieces of different heights.
+  static constexpr int RS = RS_;
   // tiles of at most NTMS 16-row subtiles whose expert has one row tile load
   // the weights non-temporally
   static constexpr int NTMS = NTMS_;
@@ -40,6 +44,10 @@ template <> struct TileCfg<96, true> { using type = TileShape<96, 16, 8, 1, 4, 4
 template <> struct TileCfg<128, true> { using type = TileShape<128, 16, 8, 1, 4, 4>; };
 template <> struct TileCfg<160, true> { using type = TileShape<160, 16, 7, 1, 4, 4>; };
 template <> struct TileCfg<192, true> { using type = TileShape<192, 16, 8, 1, 4, 4>; };
+// BM 384 (compute-heavy shapes): the 384-row tiles of the tile map are worked
+// in three 128-row pieces with 32 weight rows per wavefront, so each
+// activation fragment read from LDS feeds four MFMAs (two at BM 192).
+template <> struct TileCfg<384, true> { using type = TileShape<128, 32, 8, 1, 2, 4, 3>; };
 
 // down projection
 template <> struct TileCfg<16, false> { using type = TileShape<16, 16, 1, 4, 4, 1>; };
@@ -56,5 +64,7 @@ template <> struct TileCfg<160, false> { using type = TileShape<160, 16, 8, 1, 4
 // loads only up to 4 subtiles: on the 64-expert shapes that ran 1-3 % faster
 // than with every single-tile expert non-temporal.
 template <> struct TileCfg<192, false> { using type = TileShape<192, 32, 8, 1, 2, 4>; };
+// BM 384: two 192-row pieces, the BM 192 shape.
+template <> struct TileCfg<384, false> { using type = TileShape<192, 32, 8, 1, 2, 4, 2>; };
 
 }  // namespace moe

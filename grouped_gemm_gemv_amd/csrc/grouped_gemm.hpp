@@ -409,7 +409,7 @@ struct Gemm {
   }
 };
 
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ>
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int RS>
 __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) {
   using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, NTMS, WQ>;
   // one LDS array per activation stage (stages past NA are 16-byte stubs)
@@ -424,10 +424,10 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  // ---- which (expert, row tile, column tile) this workgroup computes
+  // ---- which (expert, row tile, piece of it, column tile) this workgroup computes
   const int NT = (p.N + G::BN - 1) / G::BN;
   const int ntiles = p.n_tiles[0];
-  const int total = ntiles * NT;
+  const int total = ntiles * NT * RS;
   const int j = blockIdx.x >> 3;
   // Skew test, identical in every workgroup: are some experts' tile counts
   // well above the mean over active experts (max * active > 2 * tiles)?
@@ -456,19 +456,25 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
     L = ((j / kXcdChunk) * 8 + (blockIdx.x & 7)) * kXcdChunk + j % kXcdChunk;
   }
   if (L >= total) return;
-  // expert e owns units [tile_off[e] * NT, tile_off[e+1] * NT)
+  // expert e owns units [tile_off[e] * NT * RS, tile_off[e+1] * NT * RS),
+  // column tile major, then row tile, then piece
   int e = 0;
   for (int b = 0; b <= p.E; b += 64) {
     const int i = b + lane;
     bool le = false;
-    if (i >= 1 && i <= p.E) le = (long long)p.tile_off[i] * NT <= (long long)L;
+    if (i >= 1 && i <= p.E) le = (long long)p.tile_off[i] * NT * RS <= (long long)L;
     e += __popcll(__ballot(le));
   }
   const int t0 = p.tile_off[e];
   const int mt = p.tile_off[e + 1] - t0;
-  const int local = L - t0 * NT;
-  const int nt = local / mt;
-  const int4 ent = reinterpret_cast<const int4*>(p.tile_map)[t0 + (local - nt * mt)];
+  const int local = L - t0 * NT * RS;
+  const int nt = local / (mt * RS);
+  const int rem = local - nt * mt * RS;
+  const int4 ent = reinterpret_cast<const int4*>(p.tile_map)[t0 + rem / RS];
+  const int piece = rem % RS;
+  const int row0 = ent.y + piece * BM;           // first row of this workgroup
+  const int rows = min(BM, ent.z - piece * BM);  // rows of this piece
+  if (rows <= 0) return;
 
   using Elt = typename G::Elt;
   typename G::Ctx c;
@@ -477,12 +483,12 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   c.ldo = (size_t)p.N * sizeof(Elt);
   c.nk = ld / kKB;
   c.nit = (c.nk + WK - 1) / WK;
-  c.rows = ent.z;
+  c.rows = rows;
   c.N = p.N;
   c.wk = wave / WN;
   const int nbase = nt * G::BN;               // first weight row of the workgroup
   c.n0 = nbase + (wave % WN) * WTN;
-  c.out = reinterpret_cast<char*>(p.out) + (size_t)ent.y * c.ldo;
+  c.out = reinterpret_cast<char*>(p.out) + (size_t)row0 * c.ldo;
   {
     char* const all[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
 #pragma unroll
@@ -490,12 +496,12 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   }
   if (p.act_rows != nullptr) {
     // activation row r of the tile is row act_rows[row0 + r] of the source
-    c.arow = p.act_rows + ent.y;
+    c.arow = p.act_rows + row0;
     c.act = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.act), (short)0, p.act_nrows * ld, 0x00020000);
   } else {
     c.arow = nullptr;
     c.act = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(reinterpret_cast<const char*>(p.act) + (size_t)ent.y * ld), (short)0, ent.z * ld, 0x00020000);
+        const_cast<char*>(reinterpret_cast<const char*>(p.act) + (size_t)row0 * ld), (short)0, rows * ld, 0x00020000);
   }
   const int ldw = WQ ? p.K : ld;               // weight row bytes (one byte per fp8 code)
   const size_t wbase = (size_t)e * p.N * ldw + (size_t)nbase * ldw;
@@ -518,18 +524,19 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
     c.scale[0] = p.s0 + (size_t)e * p.N;
     c.scale[G::NMAT - 1] = (GATED ? p.s1 : p.s0) + (size_t)e * p.N;
   }
-  G::template run_ms<G::MSUB>((ent.z + 15) >> 4, mt == 1, c);
+  // the weights are read by this workgroup alone if the expert's rows all fit in it
+  G::template run_ms<G::MSUB>((rows + 15) >> 4, mt == 1 && ent.z <= BM, c);
 }
 
 template <class Tr, class Cfg, bool GATED, bool WQ>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   constexpr int BN = Cfg::WN * Cfg::WTN;
   const int NT = (a.N + BN - 1) / BN;
-  const long long units = (long long)a.max_tiles * NT;
+  const long long units = (long long)a.max_tiles * NT * Cfg::RS;
   const long long round = a.skew_map ? 8LL * kXcdChunk : 8;  // chunked mapping: whole rounds of chunks
   const long long grid = ((units + round - 1) / round) * round;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::NTMS, WQ>),
+  hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::NTMS, WQ, Cfg::RS>),
                      dim3((unsigned)grid), dim3(64 * Cfg::WN * Cfg::WK), 0, stream, a);
   return hipGetLastError();
 }
@@ -548,6 +555,7 @@ hipError_t dispatch_bm(int BM, const GemmArgs& a, hipStream_t stream) {
     MOE_BM_CASE(128)
     MOE_BM_CASE(160)
     MOE_BM_CASE(192)
+    MOE_BM_CASE(384)
 #undef MOE_BM_CASE
     default: return hipErrorInvalidValue;
   }

@@ -59,7 +59,7 @@ def test_query_sizes_match_definition(name):
     st, q = _query(s)
     assert st == 0
     assert q.rows == O.row_space(wl.T, wl.k, wl.E, wl.capacity)
-    assert q.tile_rows in (16, 32, 48, 64, 96, 128, 160, 192)
+    assert q.tile_rows in (16, 32, 48, 64, 96, 128, 160, 192, 384)
     for p in (0, 1):
         assert q.max_tiles >= O.max_tiles(wl.T, wl.k, wl.E, wl.capacity, q.tile_rows, p)
     assert q.n_passes == (2 if wl.capacity else 1)
@@ -68,7 +68,7 @@ def test_query_sizes_match_definition(name):
 
 
 def test_tile_rows_override():
-    for bm in (16, 32, 48, 64, 96, 128, 160, 192):
+    for bm in (16, 32, 48, 64, 96, 128, 160, 192, 384):
         st, q = _query(_shape(T=300, E=16, k=4, C=40, bm=bm))
         assert st == 0 and q.tile_rows == bm
         for p in (0, 1):
@@ -77,7 +77,7 @@ def test_tile_rows_override():
 
 @pytest.mark.parametrize("name,bm", [
     ("mixtral_t512", 160),        # 8 experts x 32 down column tiles fill the units; 128 rows pad less at 160
-    ("mixtral_t4096", 192),       # 8 x 6 x 16 = 768 tiles of 192 rows: the tallest tile
+    ("mixtral_t4096", 384),       # 1024 rows per expert: 384-row tiles worked in pieces
     ("mixtral_decode_t1", 16),    # 2 active experts: split-K short tiles keep the units up
     ("mixtral_decode_t8", 16),    # two rows per active expert: 16-row split-K tiles
     ("mixtral_decode_t128", 160), # 8 experts x 32 tall down tiles fill the units
@@ -104,6 +104,8 @@ def test_automatic_tile_rows(name, bm):
     (1536, 8, 1, 3584, 2560, 192),  # 192 rows: one 192-row tile beats 160 + 32
     (2048, 8, 1, 2048, 1408, 160),  # 256 rows: 2 x 160 pads less than 2 x 192
     (3584, 8, 1, 2048, 1408, 192),  # 448 rows, 8 x 3 x 8 tiles of 192 rows
+    (8192, 8, 1, 2048, 1408, 384),  # 1024 rows per expert
+    (4096, 1, 1, 4096, 14336, 384), # one expert of 4096 rows: 22 x 16 tiles of 192 rows, then 384
 ])
 def test_tile_rows_rule_shapes(T, E, k, d, F, bm):
     st, q = _query(_shape(T=T, d=d, E=E, k=k, F=F))

@@ -56,17 +56,26 @@ CASES = {
     "bf16_t16_e64": ("mixtral_t512", dict(T=16, d=256, E=64, k=6, F=128)),
     "f32_t16_e32": ("tiny_f32", dict(T=16, E=32, k=4)),
     "bf16_t17": ("mixtral_t512", dict(T=17, d=128, F=64)),
+    # 384-row tiles, worked in pieces (three of 128 rows by gate+up, two of
+    # 192 by down): experts of two and three map tiles with ragged and empty
+    # last pieces, the capacity split, and fp32
+    "bf16_bm384": ("mixtral_t512", dict(T=900, d=128, E=2, k=1, F=192), dict(tile_rows=384)),
+    "bf16_bm384_cap": ("capacity_gini0.30", dict(T=400, d=64, E=4, k=2, F=128, capacity=150),
+                       dict(tile_rows=384)),
+    "f32_bm384": ("tiny_f32", dict(T=300, E=3, k=2, F=128), dict(tile_rows=384)),
 }
 
 
 def _workload(case):
-    base, over = CASES[case]
+    base, over = CASES[case][:2]
     return get_workload(base, **over)
 
 
-def _shape(wl):
+def _shape(wl, case=None):
     from grouped_gemm_gemv_amd import Shape
-    return Shape(T=wl.T, d=wl.d, E=wl.E, k=wl.k, F=wl.F, capacity=wl.capacity, dtype=torch_dtype(wl.dtype))
+    extra = CASES[case][2] if case is not None and len(CASES[case]) > 2 else {}
+    return Shape(T=wl.T, d=wl.d, E=wl.E, k=wl.k, F=wl.F, capacity=wl.capacity, dtype=torch_dtype(wl.dtype),
+                 **extra)
 
 
 class Run:
@@ -78,7 +87,7 @@ class Run:
         self.wl = wl
         self.inp = make_inputs(wl, seed)
         inp = self.inp
-        self.shape = _shape(wl)
+        self.shape = _shape(wl, case)
         self.q = M.query(self.shape)
         dt = torch_dtype(wl.dtype)
         self.x, self.wr = dev(inp.x), dev(inp.wr)

@@ -18,8 +18,8 @@ N_CASES = 24
 TILES = (0, 0, 0, 16, 32, 48, 64, 96, 128, 160, 192)
 
 
-def draw(i):
-    rng = np.random.default_rng(1000 + i)
+def draw(i, seed_base=1000, tiles=TILES):
+    rng = np.random.default_rng(seed_base + i)
     E = int(rng.choice([1, 2, 3, 5, 8, 12, 16, 31, 64, 100, 256]))
     k = int(rng.integers(1, min(E, 8) + 1))
     T = int(rng.choice([1, 2, 7, 15, 16, 17, 63, 100, 257, 600]))
@@ -29,17 +29,27 @@ def draw(i):
     cap = 0
     if rng.random() < 0.35:
         cap = int(rng.integers(1, max(2, T * k // max(E, 1)) + 2))
-    bm = int(rng.choice(TILES))
+    bm = int(rng.choice(tiles))
     layout = int(rng.integers(0, 2))
     return dict(E=E, k=k, T=T, d=d, F=F, kind=str(kind), capacity=cap, bm=bm, layout=layout)
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shape_parity(i):
+    _run_case(i, draw(i))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_shape_parity_384_row_tiles(i):
+    """384-row tiles: each tile of the map is worked in pieces (three of 128
+    rows by gate+up, two of 192 by down), some of them empty or ragged."""
+    _run_case(100 + i, draw(i, seed_base=2000, tiles=(384,)))
+
+
+def _run_case(i, c):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import grouped_gemm_gemv_amd as M
-    c = draw(i)
     print(f"\n[gpu random] case {i}: {c}", flush=True)
     base = {"bf16": "mixtral_t512", "f32": "tiny_f32", "fp8": "mixtral_t512_fp8"}[c["kind"]]
     over = dict(T=c["T"], d=c["d"], E=c["E"], k=c["k"], F=c["F"], capacity=c["capacity"])

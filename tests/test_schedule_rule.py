@@ -13,7 +13,7 @@ from oracle import moe_oracle as O
 from workloads import get_workload, make_inputs
 
 BM = {"mixtral_t512": 160, "e64_zipf_a0.0": 192, "e64_zipf_a1.2": 192, "e64_zipf_a2.0": 192,
-      "capacity_gini0.10": 192, "mixtral_t4096": 192}
+      "capacity_gini0.10": 192, "mixtral_t4096": 384}
 
 
 def skewed(tile_off):
