@@ -85,6 +85,16 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def gemm_role(kernel_name: str):
+    """'gateup' or 'down' for a grouped-GEMM kernel name (its sixth template
+    argument is the gated flag), else None."""
+    key = "grouped_gemm_kernel<"
+    if key not in kernel_name:
+        return None
+    args = kernel_name.split(key, 1)[1].split(">(", 1)[0].split(", ")
+    return "gateup" if args[5].strip() == "true" else "down"
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the fused gate+up GEMM from the committed PMC summary,
     if it was taken on the current GEMM sources and this workload; else None."""
@@ -152,8 +162,8 @@ def pmc_summary(fetch_db: str, write_db: str, workload: str):
         copy_kib = sum(copies) / 3
         scale = calib / copy_kib
         out[counter] = (copy_kib, scale)
-        for key, flag in (("gateup", ", true,"), ("down", ", false,")):
-            vals = [v for n, _, v in rows if "grouped_gemm_kernel" in n and flag in n]
+        for key in ("gateup", "down"):
+            vals = [v for n, _, v in rows if gemm_role(n) == key]
             out[(key, counter)] = (sum(vals) / max(1, len(vals)), len(vals))
     (cf, sf), (cw, sw) = out["FETCH_SIZE"], out["WRITE_SIZE"]
     print(f"copy_fetch_kib_per_256MiB: {cf:.1f}  (mean of the 3 calibration copies)")
