@@ -18,20 +18,28 @@
 
 namespace moe {
 
-template <int BM_, int WTN_, int WN_, int WK_, int PF_, int NTMS_ = 0, int RS_ = 1>
+template <int BM_, int WTN_, int WN_, int WK_, int PF_, int NTMS_ = 0, int RS_ = 1, int WS_ = 0>
 struct TileShape {
   static constexpr int BM = BM_, WTN = WTN_, WN = WN_, WK = WK_, PF = PF_;
   // A workgroup computes BM rows; a tile of the tile map (RS * BM rows) is
   // split into RS such pieces, so the two GEMMs can work the same tile map
   // in pieces of different heights.
   static constexpr int RS = RS_;
+  // register sets of the weight prefetch: 0 = PF + 1; or PF, where the set an
+  // iteration has just multiplied is refilled at once and each activation
+  // fragment is read from LDS just before its MFMAs (fewer registers, the
+  // same prefetch distance; the main loop unrolls PF * (PF + 1) iterations)
+  static constexpr int WS = WS_;
   // tiles of at most NTMS 16-row subtiles whose expert has one row tile load
   // the weights non-temporally
   static constexpr int NTMS = NTMS_;
 };
 
-template <int BM, bool GATED>
+// WQ: E4M3 weight codes; they take the bf16 shapes unless specialised below.
+template <int BM, bool GATED, bool WQ = false>
 struct TileCfg;
+template <int BM, bool GATED>
+struct TileCfg<BM, GATED, true> : TileCfg<BM, GATED, false> {};
 
 // gate+up (two projections per wavefront).  BM 16 (a token or two per
 // expert): 16 weight rows per wavefront give twice the workgroups of 32, which
@@ -44,6 +52,11 @@ template <> struct TileCfg<96, true> { using type = TileShape<96, 16, 8, 1, 4, 4
 template <> struct TileCfg<128, true> { using type = TileShape<128, 16, 8, 1, 4, 4>; };
 template <> struct TileCfg<160, true> { using type = TileShape<160, 16, 7, 1, 4, 4>; };
 template <> struct TileCfg<192, true> { using type = TileShape<192, 16, 8, 1, 4, 4>; };
+// E4M3 gate+up at BM 160 (T = 512 at the Mixtral shape): the matrix cores,
+// not HBM, set its time, and with half the weight registers of bf16 the
+// 32-row shape fits at 160 rows in the register-lean form; each activation
+// fragment then feeds four MFMAs instead of two (gate+up 244 vs 273 us).
+template <> struct TileCfg<160, true, true> { using type = TileShape<160, 32, 8, 1, 2, 4, 1, 2>; };
 // BM 384 (compute-heavy shapes): the 384-row tiles of the tile map are worked
 // in three 128-row pieces with 32 weight rows per wavefront, so each
 // activation fragment read from LDS feeds four MFMAs (two at BM 192).

@@ -102,7 +102,7 @@ __device__ __forceinline__ uint4 widen_e4m3(unsigned lo, unsigned hi) {
 
 // WQ: the weights are OCP E4M3 codes with one fp32 scale per output channel
 // (weight row); the activations stay bf16.
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ>
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int WS = 0>
 struct Gemm {
   using Elt = typename Tr::T;
   static_assert(!WQ || std::is_same<Tr, TBF16>::value, "fp8 weights take bf16 activations");
@@ -117,6 +117,9 @@ struct Gemm {
   static constexpr int BN = WN * WTN;             // output columns per workgroup
   static constexpr int NW = WN * WK;              // wavefronts per workgroup
   static constexpr int NA = PF + 1;               // activation stages in LDS
+  static constexpr int NWS = WS ? WS : PF + 1;     // weight register sets
+  static_assert(NWS == PF || NWS == PF + 1, "weight register sets");
+  static constexpr int UNR = NWS == NA ? NA : NA * NWS;  // iterations per unrolled round
   static constexpr int STAGE = BM * ROWB;         // bytes per activation stage
   static_assert(WTN % 16 == 0 && BM % 16 == 0 && PF >= 2 && PF <= 7, "tile shape");
 
@@ -166,7 +169,9 @@ struct Gemm {
     constexpr int QW = (NQ + NW - 1) / NW;
     constexpr int WAITN = (PF - 1) * (QW + WL);   // loads issued after iteration it's loads
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // uniform in the wavefront; saying so keeps the LDS offsets below in
+    // scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int aoff[QW];
     int lofs[QW];
 #pragma unroll
@@ -192,7 +197,7 @@ struct Gemm {
 #pragma unroll
         for (int jm = 0; jm < MS; ++jm) acc[m][i][jm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 wq[NA][WL];
+    uint4 wq[NWS][WL];
 
     auto load_w = [&](int it, uint4* dst) {
       const int s = min(it * WK + c.wk, c.nk - 1);  // clamped: values past the end are unused
@@ -235,9 +240,6 @@ struct Gemm {
       for (int h = 0; h < 2; ++h) {
         const int chunk = WQ ? 2 * (lane >> 4) + h : h * 4 + (lane >> 4);
         const int co = (chunk ^ rsw) * 16;
-        uint4 af[MS];
-#pragma unroll
-        for (int jm = 0; jm < MS; ++jm) af[jm] = *reinterpret_cast<const uint4*>(lb + jm * 16 * ROWB + co);
         uint4 wop[NMAT * NSUB];
 #pragma unroll
         for (int q = 0; q < NMAT * NSUB; ++q) {
@@ -246,17 +248,34 @@ struct Gemm {
           else
             wop[q] = w[q * 2 + h];
         }
+        if constexpr (NWS == PF) {
+          // register-lean shapes: each activation fragment is read just
+          // before its MFMAs
 #pragma unroll
-        for (int jm = 0; jm < MS; ++jm)
+          for (int jm = 0; jm < MS; ++jm) {
+            const uint4 a = *reinterpret_cast<const uint4*>(lb + jm * 16 * ROWB + co);
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m)
+            for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int i = 0; i < NSUB; ++i) acc[m][i][jm] = mma16<Tr>(wop[m * NSUB + i], af[jm], acc[m][i][jm]);
+              for (int i = 0; i < NSUB; ++i) acc[m][i][jm] = mma16<Tr>(wop[m * NSUB + i], a, acc[m][i][jm]);
+          }
+        } else {
+          uint4 af[MS];
+#pragma unroll
+          for (int jm = 0; jm < MS; ++jm) af[jm] = *reinterpret_cast<const uint4*>(lb + jm * 16 * ROWB + co);
+#pragma unroll
+          for (int jm = 0; jm < MS; ++jm)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+              for (int i = 0; i < NSUB; ++i) acc[m][i][jm] = mma16<Tr>(wop[m * NSUB + i], af[jm], acc[m][i][jm]);
+        }
       }
     };
-    // One iteration `it` (u = it mod NA, so stage and register indices are
-    // compile-time and each LDS stage is its own array: the compiler then
-    // knows loads into one stage do not alias reads of another):
+    // One iteration `it` (u = it mod UNR; stage u mod NA and weight registers
+    // u mod NWS, so the indices are compile-time and each LDS stage is its
+    // own array: the compiler then knows loads into one stage do not alias
+    // reads of another):
     //   1. wait until this wavefront's loads of iteration `it` (activation
     //      tile and weights, issued PF iterations ago) have landed; later
     //      iterations' loads stay in flight;
@@ -265,7 +284,8 @@ struct Gemm {
     //      every wavefront is done with stage (it - 1) mod NA;
     //   3. issue the activation tile of it + PF into that free stage;
     //   4. MFMAs of iteration `it`;
-    //   5. issue the weights of it + PF into the registers freed last iteration.
+    //   5. issue the weights of it + PF into the registers freed last
+    //      iteration (or, with NWS = PF, into the ones just multiplied).
     // The gate+up kernel raises the wavefront's issue priority while it issues
     // loads, so a wavefront busy with MFMAs on the same SIMD does not delay the
     // next loads (measured 1.5 % at 128 rows per expert; no gain for down).
@@ -278,10 +298,10 @@ struct Gemm {
       load_a(it + PF, c.stage[(u + PF) % NA]);
       if constexpr (GATED) __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      if (WK == 1 || it * WK + c.wk < c.nk) compute(c.stage[u], wq[u]);
+      if (WK == 1 || it * WK + c.wk < c.nk) compute(c.stage[u % NA], wq[u % NWS]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (GATED) __builtin_amdgcn_s_setprio(2);
-      load_w(it + PF, wq[(u + PF) % NA]);
+      load_w(it + PF, wq[(u + PF) % NWS]);
       if constexpr (GATED) __builtin_amdgcn_s_setprio(0);
     };
 
@@ -291,18 +311,20 @@ struct Gemm {
       load_w(u, wq[u]);
     }
     int it0 = 0;
-    for (; it0 + NA <= c.nit; it0 += NA) {
-      static_for<NA>([&](auto uc) { body(it0 + decltype(uc)::value, uc, std::integral_constant<int, WAITN>{}); });
+    for (; it0 + UNR <= c.nit; it0 += UNR) {
+      static_for<UNR>([&](auto uc) { body(it0 + decltype(uc)::value, uc, std::integral_constant<int, WAITN>{}); });
     }
-    // The last nit mod NA iterations.  Their weight loads fetch values no
-    // later iteration uses, and the compiler may drop them, so tail
-    // iteration u counts only what is surely issued after its own loads: the
-    // loop's last PF - 1 - u iterations, and the activation loads of the u
-    // tail iterations before it.  (Waiting for WAITN there could let a
-    // wavefront reach the barrier before its activation loads had landed.)
-    static_for<NA>([&](auto uc) {
+    // The last nit mod UNR iterations.  Weight loads of the tail whose values
+    // no later iteration uses may be dropped by the compiler, so tail
+    // iteration u counts only what is surely issued after its own loads:
+    // when those came from the loop (u < PF), all loads of the loop's last
+    // PF - 1 - u iterations and the activation loads of the u tail iterations
+    // before it; when they came from the tail, the activation loads of the
+    // PF - 1 tail iterations in between.  (Waiting for WAITN there could let
+    // a wavefront reach the barrier before its activation loads had landed.)
+    static_for<UNR>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
-      constexpr int n = u < PF ? (PF - 1 - u) * (QW + WL) + u * QW : 0;
+      constexpr int n = u < PF ? (PF - 1 - u) * (QW + WL) + u * QW : (PF - 1) * QW;
       if (it0 + u < c.nit) body(it0 + u, uc, std::integral_constant<int, n>{});
     });
     // the trailing (clamped) loads still write LDS: drain them before the
@@ -409,9 +431,9 @@ struct Gemm {
   }
 };
 
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int RS>
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int RS, int WS>
 __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) {
-  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, NTMS, WQ>;
+  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, NTMS, WQ, WS>;
   // one LDS array per activation stage (stages past NA are 16-byte stubs)
   __shared__ __attribute__((aligned(16))) char st0[G::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[G::STAGE];
@@ -536,7 +558,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const long long round = a.skew_map ? 8LL * kXcdChunk : 8;  // chunked mapping: whole rounds of chunks
   const long long grid = ((units + round - 1) / round) * round;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::NTMS, WQ, Cfg::RS>),
+  hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::NTMS, WQ, Cfg::RS,
+                                         Cfg::WS>),
                      dim3((unsigned)grid), dim3(64 * Cfg::WN * Cfg::WK), 0, stream, a);
   return hipGetLastError();
 }
@@ -546,7 +569,7 @@ hipError_t dispatch_bm(int BM, const GemmArgs& a, hipStream_t stream) {
   switch (BM) {
 #define MOE_BM_CASE(bm) \
   case bm:              \
-    return launch_cfg<Tr, typename TileCfg<bm, GATED>::type, GATED, WQ>(a, stream);
+    return launch_cfg<Tr, typename TileCfg<bm, GATED, WQ>::type, GATED, WQ>(a, stream);
     MOE_BM_CASE(16)
     MOE_BM_CASE(32)
     MOE_BM_CASE(48)
