@@ -77,6 +77,11 @@ template <> struct TileCfg<160, false> { using type = TileShape<160, 16, 8, 1, 4
 // loads only up to 4 subtiles: on the 64-expert shapes that ran 1-3 % faster
 // than with every single-tile expert non-temporal.
 template <> struct TileCfg<192, false> { using type = TileShape<192, 32, 8, 1, 2, 4>; };
+// E4M3 down at BM 160: 32 output columns per wavefront over 4 wavefronts
+// (one per SIMD, so the registers suffice without the lean form); the same
+// 128 columns per workgroup, half the LDS reads per MFMA (T = 512: 154 vs
+// 159 us; decode T = 256: 93 vs 102 us).
+template <> struct TileCfg<160, false, true> { using type = TileShape<160, 32, 4, 1, 4, 10>; };
 // BM 384: two 192-row pieces, the BM 192 shape.
 template <> struct TileCfg<384, false> { using type = TileShape<192, 32, 8, 1, 2, 4, 2>; };
 
