@@ -263,17 +263,30 @@ moe_status_t enqueue_permute(const moe_shape_t& s, const Plan& p, const void* x,
   return hip_status(moe::launch_gather(x, d.row_of, Tk, s.k, (int64_t)s.d * elt_bytes(s), x_perm, st));
 }
 
+// pass 0 or 1; kBothPasses: both passes of the capacity mode in one launch
+constexpr int kBothPasses = 2;
+
 moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass, bool gated) {
   moe::GemmArgs a{};
   a.act_rows = nullptr;
   a.act_nrows = 0;
-  a.tile_off = d.tile_off + pass * (s.E + 1);
-  a.tile_map = d.tile_map + (size_t)pass * d.max_tiles * 4;
-  a.n_tiles = d.n_tiles + pass;
+  const int p0 = pass == kBothPasses ? 0 : pass;
+  a.tile_off = d.tile_off + p0 * (s.E + 1);
+  a.tile_map = d.tile_map + (size_t)p0 * d.max_tiles * 4;
+  a.n_tiles = d.n_tiles + p0;
+  a.tile_off2 = nullptr;
+  a.tile_map2 = nullptr;
+  a.n_tiles2 = nullptr;
+  a.max_tiles = (int)pass_max_tiles(s, d.tile_rows, p0);
+  if (pass == kBothPasses) {
+    a.tile_off2 = d.tile_off + (s.E + 1);
+    a.tile_map2 = d.tile_map + (size_t)d.max_tiles * 4;
+    a.n_tiles2 = d.n_tiles + 1;
+    a.max_tiles += (int)pass_max_tiles(s, d.tile_rows, 1);
+  }
   a.E = s.E;
   a.K = gated ? s.d : s.F;
   a.N = gated ? s.F : s.d;
-  a.max_tiles = (int)pass_max_tiles(s, d.tile_rows, pass);
   a.skew_map = 1;
   a.blocked16 = s.weight_layout == MOE_LAYOUT_BLOCKED16 ? 1 : 0;
   return a;
@@ -341,12 +354,12 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_rou
       return MOE_ERR_HIP;
   }
   if ((st = enqueue_permute(*s, p, x, v.topk_ids, v.disp, nullptr, ws + p.ws_perm, stream)) != MOE_OK) return st;
-  const int passes = s->capacity > 0 ? 2 : 1;
-  for (int ps = 0; ps < passes; ++ps) {
-    if ((st = enqueue_gate_up(*s, nullptr, w_gate, w_up, v.disp, ps, v.h, stream, x, s_gate, s_up)) != MOE_OK)
-      return st;
-    if ((st = enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream, s_down)) != MOE_OK) return st;
-  }
+  // capacity mode: both passes in each launch (the overflow tiles of an expert
+  // run next to its first-pass tiles and find its weights in L2)
+  const int ps = s->capacity > 0 ? kBothPasses : 0;
+  if ((st = enqueue_gate_up(*s, nullptr, w_gate, w_up, v.disp, ps, v.h, stream, x, s_gate, s_up)) != MOE_OK)
+    return st;
+  if ((st = enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream, s_down)) != MOE_OK) return st;
   return hip_status(
       moe::launch_combine(s->dtype, v.y_perm, v.topk_w, v.disp.row_of, s->T, s->k, s->d, out, stream));
 }

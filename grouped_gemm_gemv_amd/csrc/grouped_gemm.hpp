@@ -447,8 +447,12 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   const int wave = threadIdx.x >> 6;
 
   // ---- which (expert, row tile, piece of it, column tile) this workgroup computes
+  // (with a second pass merged in, an expert's tiles are its first-pass tiles
+  // followed by its overflow tiles, and its tile offset is the sum of both)
+  const bool two = p.tile_off2 != nullptr;
+  auto tiles_before = [&](int i) { return p.tile_off[i] + (two ? p.tile_off2[i] : 0); };
   const int NT = (p.N + G::BN - 1) / G::BN;
-  const int ntiles = p.n_tiles[0];
+  const int ntiles = p.n_tiles[0] + (two ? p.n_tiles2[0] : 0);
   const int total = ntiles * NT * RS;
   const int j = blockIdx.x >> 3;
   // Skew test, identical in every workgroup: are some experts' tile counts
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
     int mx = 0, act = 0;
     for (int b = 0; b < p.E; b += 64) {
       const int i = b + lane;
-      const int t = (i < p.E) ? p.tile_off[i + 1] - p.tile_off[i] : 0;
+      const int t = (i < p.E) ? tiles_before(i + 1) - tiles_before(i) : 0;
       mx = max(mx, t);
       act += __popcll(__ballot(t > 0));
     }
@@ -478,21 +482,24 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
     L = ((j / kXcdChunk) * 8 + (blockIdx.x & 7)) * kXcdChunk + j % kXcdChunk;
   }
   if (L >= total) return;
-  // expert e owns units [tile_off[e] * NT * RS, tile_off[e+1] * NT * RS),
+  // expert e owns units [tiles_before(e) * NT * RS, tiles_before(e+1) * NT * RS),
   // column tile major, then row tile, then piece
   int e = 0;
   for (int b = 0; b <= p.E; b += 64) {
     const int i = b + lane;
     bool le = false;
-    if (i >= 1 && i <= p.E) le = (long long)p.tile_off[i] * NT * RS <= (long long)L;
+    if (i >= 1 && i <= p.E) le = (long long)tiles_before(i) * NT * RS <= (long long)L;
     e += __popcll(__ballot(le));
   }
-  const int t0 = p.tile_off[e];
-  const int mt = p.tile_off[e + 1] - t0;
+  const int t0 = tiles_before(e);
+  const int mt = tiles_before(e + 1) - t0;
   const int local = L - t0 * NT * RS;
   const int nt = local / (mt * RS);
   const int rem = local - nt * mt * RS;
-  const int4 ent = reinterpret_cast<const int4*>(p.tile_map)[t0 + rem / RS];
+  const int ti = rem / RS;                            // tile of the expert
+  const int mt1 = p.tile_off[e + 1] - p.tile_off[e];  // of them in the first pass
+  const int4 ent = ti < mt1 ? reinterpret_cast<const int4*>(p.tile_map)[p.tile_off[e] + ti]
+                            : reinterpret_cast<const int4*>(p.tile_map2)[p.tile_off2[e] + ti - mt1];
   const int piece = rem % RS;
   const int row0 = ent.y + piece * BM;           // first row of this workgroup
   const int rows = min(BM, ent.z - piece * BM);  // rows of this piece

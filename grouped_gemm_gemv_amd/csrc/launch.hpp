@@ -78,8 +78,14 @@ struct GemmArgs {
   const int32_t* tile_off;   // [E+1] of this pass
   const int32_t* tile_map;   // [max_tiles][4] of this pass
   const int32_t* n_tiles;    // [1] of this pass
+  // Both passes of the capacity mode in one launch: the overflow pass's tile
+  // offsets, map and count (else null).  Each expert's overflow tiles follow
+  // its first-pass tiles, so both read its weights while they are in L2.
+  const int32_t* tile_off2;
+  const int32_t* tile_map2;
+  const int32_t* n_tiles2;
   int E, K, N;
-  int max_tiles;
+  int max_tiles;             // tiles of the map(s) the grid must cover
   int skew_map;              // 1: uneven tile counts per expert deal chunks of units to the XCDs in turn
   int blocked16;             // 1: weights in 16-row blocked order (moe_weight_layout_t)
 };
