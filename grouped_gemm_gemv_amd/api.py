@@ -127,6 +127,8 @@ def moe_ffn_gate_up_gather(shape: Shape, x, w_gate, w_up, disp: Dispatch, pass_i
 
 LAYOUT_ROWS = 0
 LAYOUT_BLOCKED16 = 1
+# pass argument of the grouped GEMM calls: both passes of the capacity mode in one launch
+PASS_BOTH = 2
 
 
 def moe_pack_blocked16(src, dst=None, stream=None):

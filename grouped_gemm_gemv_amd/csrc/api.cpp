@@ -264,12 +264,13 @@ moe_status_t enqueue_permute(const moe_shape_t& s, const Plan& p, const void* x,
 }
 
 // pass 0 or 1; kBothPasses: both passes of the capacity mode in one launch
-constexpr int kBothPasses = 2;
+constexpr int kBothPasses = MOE_PASS_BOTH;
 
 moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass, bool gated) {
   moe::GemmArgs a{};
   a.act_rows = nullptr;
   a.act_nrows = 0;
+  const bool both = pass == kBothPasses && s.capacity > 0;
   const int p0 = pass == kBothPasses ? 0 : pass;
   a.tile_off = d.tile_off + p0 * (s.E + 1);
   a.tile_map = d.tile_map + (size_t)p0 * d.max_tiles * 4;
@@ -278,7 +279,7 @@ moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass,
   a.tile_map2 = nullptr;
   a.n_tiles2 = nullptr;
   a.max_tiles = (int)pass_max_tiles(s, d.tile_rows, p0);
-  if (pass == kBothPasses) {
+  if (both) {
     a.tile_off2 = d.tile_off + (s.E + 1);
     a.tile_map2 = d.tile_map + (size_t)d.max_tiles * 4;
     a.n_tiles2 = d.n_tiles + 1;
@@ -431,7 +432,7 @@ moe_status_t moe_ffn_gate_up(const moe_shape_t* s, const void* x_perm, const voi
   moe_status_t st = validate(s);
   if (st != MOE_OK) return st;
   if (!x_perm || !w_gate || !w_up || !h) return MOE_ERR_NULL_PTR;
-  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
+  if (pass < 0 || pass > kBothPasses) return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(*s);
   if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
   return enqueue_gate_up(*s, x_perm, w_gate, w_up, *disp, pass, h, stream);
@@ -442,7 +443,7 @@ moe_status_t moe_ffn_gate_up_gather(const moe_shape_t* s, const void* x, const v
   moe_status_t st = validate(s);
   if (st != MOE_OK) return st;
   if (!x || !w_gate || !w_up || !h) return MOE_ERR_NULL_PTR;
-  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
+  if (pass < 0 || pass > kBothPasses) return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(*s);
   if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
   return enqueue_gate_up(*s, nullptr, w_gate, w_up, *disp, pass, h, stream, x);
@@ -453,7 +454,7 @@ moe_status_t moe_ffn_down(const moe_shape_t* s, const void* h, const void* w_dow
   moe_status_t st = validate(s);
   if (st != MOE_OK) return st;
   if (!h || !w_down || !y_perm) return MOE_ERR_NULL_PTR;
-  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
+  if (pass < 0 || pass > kBothPasses) return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(*s);
   if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
   return enqueue_down(*s, h, w_down, *disp, pass, y_perm, stream);
@@ -514,7 +515,7 @@ moe_status_t moe_ffn_gate_up_fp8(const moe_shape_t* s, const void* x, const uint
   if (st != MOE_OK) return st;
   if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!x || !w_gate || !w_up || !s_gate || !s_up || !h) return MOE_ERR_NULL_PTR;
-  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
+  if (pass < 0 || pass > kBothPasses) return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(*s);
   if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
   return enqueue_gate_up(*s, nullptr, w_gate, w_up, *disp, pass, h, stream, x, s_gate, s_up);
@@ -526,7 +527,7 @@ moe_status_t moe_ffn_down_fp8(const moe_shape_t* s, const void* h, const uint8_t
   if (st != MOE_OK) return st;
   if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!h || !w_down || !s_down || !y_perm) return MOE_ERR_NULL_PTR;
-  if (pass < 0 || pass > 1) return MOE_ERR_INVALID_ARG;
+  if (pass < 0 || pass > kBothPasses) return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(*s);
   if ((st = check_dispatch(*s, p, disp)) != MOE_OK) return st;
   return enqueue_down(*s, h, w_down, *disp, pass, y_perm, stream, s_down);

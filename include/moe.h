@@ -81,7 +81,7 @@ typedef struct moe_shape {
   int32_t dtype;    /* moe_dtype_t                             */
   int32_t tile_rows;/* row-tile height of the grouped GEMMs: 0 lets the
                        library choose; else one of 16, 32, 48, 64, 96,
-                       128, 160, 192 (others: MOE_ERR_UNSUPPORTED)      */
+                       128, 160, 192, 384 (others: MOE_ERR_UNSUPPORTED) */
   int32_t weight_layout; /* moe_weight_layout_t of the expert weights
                        (the router weights are always row-major)        */
 } moe_shape_t;
@@ -105,7 +105,12 @@ typedef struct moe_sizes {
 /* Dispatch metadata (device arrays), produced by moe_permute and read by the
  * grouped FFN and the combine.  Entry f = t*k + j names slot j of token t.
  * Pass 0 is the uncapped row space or the fixed region; pass 1 the overflow
- * region (empty when uncapped). */
+ * region (empty when uncapped).  The grouped GEMM calls take pass 0, 1 or
+ * MOE_PASS_BOTH: both passes in one launch, each expert's overflow tiles
+ * next to its first-pass tiles so that they read its weights from L2 (what
+ * moe_forward runs in capacity mode); results are bitwise those of the two
+ * separate calls, and without capacity it is pass 0. */
+#define MOE_PASS_BOTH 2
 typedef struct moe_dispatch {
   int32_t* counts;         /* [E]      n_e: entries routed to expert e           */
   int32_t* offsets;        /* [E+1]    exclusive scan of counts                  */
@@ -167,7 +172,7 @@ moe_status_t moe_permute(const moe_shape_t* s, const void* x, const int32_t* top
  * SiLU in registers, no gate/up intermediates in memory):
  *   h[r, n] = silu(g) * u,  g = sum_i x_perm[r,i] * w_gate[e,n,i],
  *             u = sum_i x_perm[r,i] * w_up[e,n,i],  silu(z) = z / (1 + exp(-z))
- * for every row r of every tile (e, ...) of pass `pass` (0 or 1).
+ * for every row r of every tile (e, ...) of pass `pass` (0, 1 or MOE_PASS_BOTH).
  * x_perm [R,d]; w_gate, w_up [E,F,d]; h [R,F]; h is rounded to dtype. */
 moe_status_t moe_ffn_gate_up(const moe_shape_t* s, const void* x_perm, const void* w_gate,
                              const void* w_up, const moe_dispatch_t* disp, int pass, void* h,

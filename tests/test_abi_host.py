@@ -175,7 +175,10 @@ def test_carve_and_workspace_checks():
     d2 = MoeDispatch.from_buffer_copy(d)
     d2.max_tiles = 0
     assert lib.moe_ffn_down(ctypes.byref(s), fake, fake, ctypes.byref(d2), 0, fake, None) == 1
-    assert lib.moe_ffn_down(ctypes.byref(s), fake, fake, ctypes.byref(d), 2, fake, None) == 1
+    # pass: 0, 1 or MOE_PASS_BOTH (2); anything else is rejected before any launch
+    for bad in (-1, 3):
+        assert lib.moe_ffn_down(ctypes.byref(s), fake, fake, ctypes.byref(d), bad, fake, None) == 1
+        assert lib.moe_ffn_gate_up(ctypes.byref(s), fake, fake, fake, ctypes.byref(d), bad, fake, None) == 1
 
 
 def test_views_struct_layout():

@@ -354,6 +354,25 @@ def test_invalid_ids_flagged_and_skipped():
     assert np.array_equal(bits(out), bits(x))
 
 
+@pytest.mark.parametrize("case", ["bf16_capacity", "f32_capacity", "bf16_bm384_cap", "bf16_cap_c1",
+                                  "bf16_cap_no_spill", "bf16_ragged"])
+def test_both_passes_in_one_launch(runs, case):
+    """pass = PASS_BOTH (each expert's overflow tiles in the same launch as its
+    first-pass tiles) gives h and y bitwise equal to the two separate passes;
+    without capacity it is pass 0."""
+    import grouped_gemm_gemv_amd as M
+    r = runs(case)
+    h2, y2, h3 = torch.zeros_like(r.h), torch.zeros_like(r.y), torch.zeros_like(r.h)
+    M.moe_ffn_gate_up(r.shape, r.xp, r.wg, r.wu, r.disp, M.PASS_BOTH, h2)
+    M.moe_ffn_down(r.shape, h2, r.wd, r.disp, M.PASS_BOTH, y2)
+    M.moe_ffn_gate_up_gather(r.shape, r.x, r.wg, r.wu, r.disp, M.PASS_BOTH, h3)
+    torch.cuda.synchronize()
+    live = r.ref_disp["token_of"] >= 0
+    assert np.array_equal(bits(h2)[live], bits(r.h)[live])
+    assert np.array_equal(bits(y2)[live], bits(r.y)[live])
+    assert np.array_equal(bits(h3)[live], bits(r.h)[live])
+
+
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_gate_up_gather_equals_gate_up(runs, case):
     """The gather folded into the gate+up loads gives h bitwise equal to
