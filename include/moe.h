@@ -167,7 +167,7 @@ moe_status_t moe_permute(const moe_shape_t* s, const void* x, const int32_t* top
                          const moe_dispatch_t* disp, void* x_perm, void* workspace, size_t ws_bytes,
                          hipStream_t stream);
 
-/* Fused gate+up SwiGLU grouped GEMM over one pass's tile map (TritonMoE
+/* Fused gate+up SwiGLU grouped GEMM over a pass's tile map (TritonMoE
  * review, key machinery: both projections from one load of each input tile,
  * SiLU in registers, no gate/up intermediates in memory):
  *   h[r, n] = silu(g) * u,  g = sum_i x_perm[r,i] * w_gate[e,n,i],
@@ -186,7 +186,7 @@ moe_status_t moe_ffn_gate_up_gather(const moe_shape_t* s, const void* x, const v
                                     const void* w_up, const moe_dispatch_t* disp, int pass, void* h,
                                     hipStream_t stream);
 
-/* Down-projection grouped GEMM over one pass's tile map (TritonMoE review,
+/* Down-projection grouped GEMM over a pass's tile map (TritonMoE review,
  * desk-editor letter: the down projection is a separate kernel):
  *   y_perm[r, o] = sum_n h[r,n] * w_down[e,o,n]
  * h [R,F]; w_down [E,d,F]; y_perm [R,d] (rounded to dtype). */
