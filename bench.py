@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral_t512")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak probes (streaming read / copy, bf16 MFMA loop)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the workload the CPU oracle runs (0: all)")
     ap.add_argument("--kernel-iters", type=int, default=40)
@@ -344,6 +346,59 @@ def gemm_work(wl, counts, dt_bytes, spill_counts=None):
     return gu_flops, gu_bytes, dn_flops, dn_bytes, active
 
 
+def measured_peaks():
+    """Achievable ceilings on this device, from the probes of libmoe_peaks
+    (include/moe_peaks.h): a streaming read of 4 GiB, a copy of 1 GiB and a
+    loop of independent bf16 MFMAs, each the best over several workgroup
+    counts (and, for read and copy, chunk orders and cache policies), each
+    timed with HIP events on the stream it runs on.  The copy and the MFMA
+    results are checked exactly."""
+    import torch
+
+    from grouped_gemm_gemv_amd import peaks as P
+    cur = torch.cuda.current_stream()
+
+    def seconds(fn, n=10):
+        fn()
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        cur.synchronize()
+        a.record(cur)
+        for _ in range(n):
+            fn()
+        b.record(cur)
+        b.synchronize()
+        return a.elapsed_time(b) / n * 1e-3
+
+    nb = 4 << 30
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    sweep = [(blk, fl) for fl in range(4) for blk in (256, 512, 1024, 2048)]
+    read = max(nb / seconds(lambda: P.moe_peak_read(buf, sink, blk, fl)) / 1e9 for blk, fl in sweep)
+    del buf
+    half = 1 << 30
+    src = torch.empty(half, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.zeros_like(src)
+    copy = max(2 * half / seconds(lambda: P.moe_peak_copy(src, dst, blk, fl)) / 1e9 for blk, fl in sweep)
+    assert torch.equal(src, dst), "copy probe: wrong result"
+    del src, dst
+    iters = 8192
+    fs = torch.empty(4 * 2048, dtype=torch.float32, device="cuda")
+    mfma = 0.0
+    for blk in (512, 1024, 2048):
+        fl = float(blk) * P.MFMA_WAVES * P.MFMA_CHAINS * iters * P.MFMA_FLOPS
+        t = seconds(lambda: P.moe_peak_mfma(1.0, 1.0, iters, fs, blk))
+        assert bool((fs[:4 * blk] == 256.0 * iters).all()), "mfma probe: wrong result"
+        mfma = max(mfma, fl / t / 1e12)
+    torch.cuda.synchronize()
+    return {"hbm_read_GBps": round(read, 1), "hbm_copy_GBps": round(copy, 1), "mfma_bf16_TFLOPs": round(mfma, 1),
+            "probes": "libmoe_peaks: streaming read of 4 GiB and copy of 1 GiB (read + written bytes), best "
+                      "over 256-2048 workgroups, strided or per-wavefront chunk order, default or non-temporal "
+                      "cache policy; 8 independent bf16 16x16x32 MFMA chains per wavefront, best over "
+                      "512-2048 workgroups"}
+
+
 def cpu_baseline(wl, inp, sample_tokens):
     """The oracle as it stands on the workload (or its first `sample_tokens`
     tokens), repeated until about 12 s of CPU time have been spent."""
@@ -529,6 +584,8 @@ def main():
               "p90": round(float(np.percentile(per, 90)), 4)}
 
 
+    peaks = None if args.no_peaks else measured_peaks()
+
     gu_flops, gu_bytes, dn_flops, dn_bytes, active = gemm_work(wl, counts, dt_bytes, spill_counts)
     peak_f = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -545,6 +602,13 @@ def main():
     roof["us_per_launch"] = round(t_gu, 2)  # one launch (both passes in capacity mode)
     roof["algorithmic_bytes"] = gu_bytes
     roof["algorithmic_flops"] = gu_flops
+    if peaks is not None:
+        # the same kernel against the ceiling measured on this device
+        ach_peak = peaks["hbm_read_GBps"] if roof["bound"] == "hbm" else (
+            peaks["mfma_bf16_TFLOPs"] if wl.dtype == "bf16" else None)
+        if ach_peak:
+            roof["achievable_peak"] = ach_peak
+            roof["frac_of_achievable"] = round(ach / ach_peak, 4)
     t_gemm = (t_gu + t_dn) * 1e-6
     gemm_flops = gu_flops + dn_flops
     gemm_bytes = gu_bytes + dn_bytes
@@ -557,6 +621,10 @@ def main():
         "roofline_frac": round(max(gemm_flops / (peak_f * 1e12), gemm_bytes / (PEAK_HBM_GBS * 1e9)) / t_gemm, 4),
         "active_experts": active,
     }
+    if peaks is not None:
+        gg["hbm_frac_of_achievable"] = round(gemm_bytes / t_gemm / 1e9 / peaks["hbm_read_GBps"], 4)
+        if wl.dtype == "bf16":
+            gg["mfma_frac_of_achievable"] = round(gemm_flops / t_gemm / 1e12 / peaks["mfma_bf16_TFLOPs"], 4)
     tokens_per_s = wl.T / (ms * 1e-3)
     res = {
         "metric": METRIC,
@@ -581,6 +649,8 @@ def main():
                         "down": round(t_dn, 1), "combine": round(t_comb, 1)},
         "roofline": roof,
     }
+    if peaks is not None:
+        res["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_sample_tokens)

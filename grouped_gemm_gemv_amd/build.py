@@ -1,4 +1,5 @@
-"""Build libmoe.so in-tree with hipcc for gfx950.
+"""Build libmoe.so (the layer) and libmoe_peaks.so (measurement probes)
+in-tree with hipcc for gfx950.
 
     python -m grouped_gemm_gemv_amd.build
 
@@ -20,9 +21,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PEAKS_LIB = os.path.join(PKG, "libmoe_peaks.so")
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "gemm_bf16_gateup.hip", "gemm_bf16_down.hip",
            "gemm_f32_gateup.hip", "gemm_f32_down.hip", "gemm_fp8w_gateup.hip", "gemm_fp8w_down.hip", "layout.hip"]
+PEAKS_SOURCES = ["peaks.hip"]
 
 
 def hipcc() -> str:
@@ -50,18 +53,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 

@@ -243,3 +243,39 @@ def test_query_random_and_extreme_shapes():
         assert q.forward_ws_bytes >= q.rows * (sh["d"] + sh["F"]) * 2 + q.dispatch_bytes
         assert q.forward_ws_bytes < 2 ** 62
     assert ok > 100
+
+
+# ---- measurement probes (libmoe_peaks) ----
+
+PEAKS_HEADER = os.path.join(ROOT, "include", "moe_peaks.h")
+
+
+def test_every_declared_probe_is_exported():
+    from grouped_gemm_gemv_amd import peaks as P
+    if not os.path.exists(P.LIB_PATH):
+        pytest.skip("libmoe_peaks.so not built")
+    names = sorted(set(re.findall(r"^\s*int\s+(moe_\w+)\s*\(", open(PEAKS_HEADER).read(), re.M)))
+    assert names == sorted(P.EXPORTED)
+    lib = P.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_probe_argument_checks_return_before_any_launch():
+    from grouped_gemm_gemv_amd import peaks as P
+    if not os.path.exists(P.LIB_PATH):
+        pytest.skip("libmoe_peaks.so not built")
+    lib = P.lib()
+    fake = 1 << 20  # never dereferenced: every call below fails validation first
+    assert lib.moe_peak_read(None, 1024, fake, 1, 0, None) == 1
+    assert lib.moe_peak_read(fake, 1000, fake, 1, 0, None) == 1      # not a multiple of 1 KB
+    assert lib.moe_peak_read(fake, 0, fake, 1, 0, None) == 1
+    assert lib.moe_peak_read(fake, 1024, fake, 0, 0, None) == 1      # no workgroups
+    assert lib.moe_peak_read(fake + 8, 1024, fake, 1, 0, None) == 1  # misaligned
+    assert lib.moe_peak_read(fake, 1024, fake, 1, 4, None) == 1      # unknown flags
+    assert lib.moe_peak_read(fake, 1024, fake, 1, -1, None) == 1
+    assert lib.moe_peak_copy(fake, fake + 512, 1024, 1, 0, None) == 1  # overlapping
+    assert lib.moe_peak_copy(fake, None, 1024, 1, 0, None) == 1
+    assert lib.moe_peak_copy(fake, fake + 4096, 1024, 1, 7, None) == 1
+    assert lib.moe_peak_mfma(1.0, 1.0, 0, fake, 1, None) == 1
+    assert lib.moe_peak_mfma(1.0, 1.0, 1, None, 1, None) == 1
