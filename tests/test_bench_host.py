@@ -1,6 +1,7 @@
-"""Host-side helpers of bench.py: which launches are the gate+up and down
-GEMMs (the traffic and trace summaries depend on it), and the source hash
-that ties a committed traffic summary to the kernels it was taken on."""
+"""Host-side behaviour of bench.py: which launches are the gate+up and down
+GEMMs (the traffic and trace summaries depend on it), the source hash that
+ties a committed traffic summary to the kernels it was taken on, and the
+refusal of more than one GPU."""
 import os
 import shutil
 
@@ -37,3 +38,13 @@ def test_gemm_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.gemm_source_hash() == h0
     tiles.write_text(text.replace("TileShape<160, 16, 7, 1, 4, 4>", "TileShape<160, 16, 7, 1, 5, 4>", 1))
     assert bench.gemm_source_hash() != h0
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
