@@ -14,7 +14,7 @@ from workloads import get_workload, make_inputs
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-N_CASES = 24
+N_CASES = 96
 TILES = (0, 0, 0, 16, 32, 48, 64, 96, 128, 160, 192)
 
 
@@ -39,7 +39,7 @@ def test_random_shape_parity(i):
     _run_case(i, draw(i))
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(24))
 def test_random_shape_parity_384_row_tiles(i):
     """384-row tiles: each tile of the map is worked in pieces (three of 128
     rows by gate+up, two of 192 by down), some of them empty or ragged."""
