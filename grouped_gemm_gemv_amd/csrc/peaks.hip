@@ -40,8 +40,9 @@ __device__ __forceinline__ void st(char* p, u32x4 v) {
     *reinterpret_cast<u32x4*>(p) = v;
 }
 
-// Visits every chunk of this wavefront: f(first chunk, PF) for whole rounds
-// of chunks first, first + step, ..., then f(chunk, 1) one at a time.
+// Calls f(c, step, N) to move chunks c, c + step, ..., c + (N-1) step of
+// this wavefront: N = PF for the whole rounds, then N = 1 for the chunks
+// left over.
 template <bool REGION, int PF, class F>
 __device__ __forceinline__ void for_chunks(size_t nch, F&& f) {
   const size_t nw = (size_t)gridDim.x * kReadWaves;
