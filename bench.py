@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--summarize", metavar="DB", help="print a text summary of a rocprofv3 result database and exit")
     ap.add_argument("--kernel-table", nargs=3, metavar=("FETCH_DB", "WRITE_DB", "TRACE_DB"),
                     help="per kernel: HBM bytes per dispatch from a FETCH_SIZE and a WRITE_SIZE run (both with "
-                         "--pmc-calibration), mean duration from a kernel trace, achieved GB/s; then exit")
+                         "--pmc-calibration), median duration from a kernel trace, achieved GB/s; then exit")
     ap.add_argument("--cost-curve", action="store_true",
                     help="per-expert cost curve: time the grouped GEMMs with every expert given n rows, "
                          "for n from 1 to 1024, fit t = max(a, c + b*n) and exit")
@@ -187,7 +187,7 @@ def pmc_summary(fetch_db: str, write_db: str, workload: str):
 
 def kernel_table(fetch_db: str, write_db: str, trace_db: str):
     """Achieved HBM bandwidth of every kernel: counter bytes per dispatch
-    (scaled by the calibration copies, as in pmc_summary) over the mean
+    (scaled by the calibration copies, as in pmc_summary) over the median
     duration of the same kernel in a kernel-trace run of the same command."""
     import collections
     import sqlite3
@@ -209,7 +209,7 @@ def kernel_table(fetch_db: str, write_db: str, trace_db: str):
     dur = collections.defaultdict(list)
     for n, d in db.execute("select name, end - start from kernels"):
         dur[n].append(d)
-    print("# kernel | HBM read MB | HBM write MB | mean us (trace) | GB/s")
+    print("# kernel | HBM read MB | HBM write MB | median us (trace) | GB/s")
     for n in sorted(fetch, key=lambda k: -(fetch[k] + write.get(k, 0))):
         if n not in dur or "copyBuffer" in n:
             continue
