@@ -100,8 +100,8 @@ def dispatch(ids, E: int, capacity: int, tile_rows: int) -> Dict[str, list]:
             "token_of": token_of, "R": R, "tile_off": tile_off, "tile_map": tile_map}
 
 
-def expert(xrow, wg, wu, wd):
-    """One token through one SwiGLU expert with explicit loops."""
+def hidden(xrow, wg, wu):
+    """The SwiGLU intermediate of one token for one expert, with explicit loops."""
     F, d = len(wg), len(xrow)
     h = []
     for n in range(F):
@@ -111,6 +111,13 @@ def expert(xrow, wg, wu, wd):
             g += float(wg[n][i]) * float(xrow[i])
             u += float(wu[n][i]) * float(xrow[i])
         h.append(g / (1.0 + math.exp(-g)) * u)
+    return h
+
+
+def expert(xrow, wg, wu, wd):
+    """One token through one SwiGLU expert with explicit loops."""
+    F = len(wg)
+    h = hidden(xrow, wg, wu)
     y = []
     for o in range(len(wd)):
         s = 0.0

@@ -69,6 +69,9 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
 
 
+_E4M3_VALUES = e4m3_to_f64(np.arange(256, dtype=np.uint8))
+
+
 class Fp8Weights:
     """Expert weights stored as E4M3 codes with one scale per output channel.
 
@@ -88,8 +91,11 @@ class Fp8Weights:
         return self.codes.shape
 
     def expert(self, e: int) -> np.ndarray:
-        """W[e] in float64 (every product of a code value and an fp32 scale is exact)."""
-        return self.scales[e].astype(np.float64)[:, None] * e4m3_to_f64(self.codes[e])
+        """W[e] in float64 (every product of a code value and an fp32 scale is exact).
+
+        The codes are looked up in the values of all 256 codes, each from
+        e4m3_to_f64: the same definition, evaluated once per code value."""
+        return self.scales[e].astype(np.float64)[:, None] * _E4M3_VALUES[self.codes[e]]
 
 
 def widen_expert(w, e: int, dtype: str) -> np.ndarray:
@@ -323,15 +329,38 @@ def silu(z: np.ndarray) -> np.ndarray:
     return out
 
 
+def swiglu_hidden(X: np.ndarray, wg: np.ndarray, wu: np.ndarray) -> np.ndarray:
+    """One expert's SwiGLU intermediate: h = silu(Wg . x) * (Wu . x) for every row x of X.
+
+    X [n, d], wg/wu [F, d], all float64.  No biases.
+    """
+    G = X @ wg.T
+    U = X @ wu.T
+    return silu(G) * U
+
+
 def swiglu_ffn(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
     """One expert: y = Wd . (silu(Wg . x) * (Wu . x)) for every row x of X.
 
     X [n, d], wg/wu [F, d], wd [d, F], all float64.  No biases.
     """
-    G = X @ wg.T
-    U = X @ wu.T
-    H = silu(G) * U
-    return H @ wd.T
+    return swiglu_hidden(X, wg, wu) @ wd.T
+
+
+def expert_rows(x, wg, wu, wd, dtype: str, disp, e: int):
+    """Every live row of expert e with its intermediate and output.
+
+    Returns (rows, h, y): the rows of the row space that expert e's entries
+    occupy, in stable order (its fixed-region rows, then its overflow rows in
+    capacity mode), h[i] = silu(Wg[e] . x) * (Wu[e] . x) and y[i] = Wd[e] . h[i]
+    for x the token of rows[i], in float64 (no intermediate rounding).
+    """
+    tok = np.asarray(disp["token_of"])
+    base, nrows = disp["pass_base"], disp["pass_rows"]
+    rows = np.concatenate([base[p][e] + np.arange(nrows[p][e]) for p in range(2)]).astype(np.int64)
+    X = to_f64(np.asarray(x)[tok[rows]], dtype)
+    h = swiglu_hidden(X, widen_expert(wg, e, dtype), widen_expert(wu, e, dtype))
+    return rows, h, h @ widen_expert(wd, e, dtype).T
 
 
 def expert_outputs(x, wg, wu, wd, dtype: str, disp, ids) -> np.ndarray:

@@ -379,6 +379,27 @@ def test_forward_tokens_matches_forward():
     np.testing.assert_allclose(o, r["out"][toks], rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("C", [0, 3])
+def test_expert_rows_match_brute(C):
+    # every live row of each expert, in stable order, with h and y of its token
+    rng = np.random.default_rng(22 + C)
+    x, wr, wg, wu, wd = _tiny_inputs(rng, 11, 6, 4, 5)
+    r = O.forward(x, wr, wg, wu, wd, 2, "f32", capacity=C)
+    disp = r["disp"]
+    flat = r["ids"].reshape(-1)
+    for e in range(4):
+        rows, h, y = O.expert_rows(x, wg, wu, wd, "f32", disp, e)
+        fs = [f for f in range(flat.size) if flat[f] == e]          # ascending f: the stable order
+        assert rows.tolist() == [int(disp["row_of"][f]) for f in fs]
+        for i, f in enumerate(fs):
+            xr = x[f // 2].astype(np.float64)
+            hb = brute.hidden(xr, wg[e].astype(np.float64), wu[e].astype(np.float64))
+            yb = brute.expert(xr, wg[e].astype(np.float64), wu[e].astype(np.float64), wd[e].astype(np.float64))
+            np.testing.assert_allclose(h[i], hb, rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(y[i], yb, rtol=1e-11, atol=1e-13)
+            np.testing.assert_array_equal(y[i], r["y"][rows[i]])
+
+
 def test_bf16_decode_matches_torch():
     torch = pytest.importorskip("torch")
     bits = np.arange(0, 2**16, 7, dtype=np.uint16)
@@ -445,6 +466,19 @@ def _fp8_pair(rng, E, N, K):
     eb = p + q[:, :, None] + 127                         # bf16 exponent field of the value
     bits = np.where(zero, 0, (s << 15) | (eb << 7) | (m << 4)).astype(np.uint16)
     return O.Fp8Weights(codes, scales), bits
+
+
+def test_fp8_expert_table_equals_the_definition():
+    # Fp8Weights looks codes up in the values of all 256 codes: the same as
+    # decoding every code with e4m3_to_f64 (NaN codes included)
+    rng = np.random.default_rng(23)
+    codes = rng.integers(0, 256, size=(2, 16, 40), dtype=np.uint8)
+    codes[1].reshape(-1)[:256] = np.arange(256, dtype=np.uint8)
+    scales = rng.random((2, 16)).astype(np.float32)
+    w = O.Fp8Weights(codes, scales)
+    for e in range(2):
+        direct = scales[e].astype(np.float64)[:, None] * O.e4m3_to_f64(codes[e])
+        np.testing.assert_array_equal(w.expert(e), direct)
 
 
 def test_fp8_forward_equals_bf16_on_same_values():
