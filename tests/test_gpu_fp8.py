@@ -3,7 +3,8 @@ output channel, bf16 activations) against the oracle's dequantised weights.
 
 Small cases span several row and column tiles, ragged tails, every tile
 height family (split-K short tiles, 96, the 112-column 160 tile, 192),
-capacity mode and skewed routing; full-size cases check sampled tokens.
+capacity mode and skewed routing; full-size cases check every token, and h
+and y_perm on every row of the busiest expert.
 Tolerance: max|gpu - oracle| / max|oracle| <= 2e-2 (bf16 activations; the
 oracle uses the same quantised weights, so quantisation error is not part
 of the comparison).
@@ -12,7 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import moe_oracle as O
-from tests.gpu_helpers import TOL, bits, check_dispatch, dev, host64, rel_err
+from tests.gpu_helpers import TOL, bits, check_dispatch, check_routing, dev, host64, rel_err
 from workloads import get_workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -125,7 +126,8 @@ def test_fp8_rejects_f32_activations():
                           torch.ones((8, 2), device="cuda"), c, c, c, s, s, s, torch.empty_like(x), ws)
 
 
-FULL = ["mixtral_t512_fp8", "mixtral_decode_t1_fp8", "mixtral_decode_t128_fp8"]
+FULL = ["mixtral_t512_fp8", "mixtral_decode_t1_fp8", "mixtral_decode_t8_fp8", "mixtral_decode_t32_fp8",
+        "mixtral_decode_t128_fp8", "mixtral_decode_t256_fp8"]
 
 
 @pytest.fixture(scope="module")
@@ -152,9 +154,19 @@ def test_fp8_fullsize(full_weights, name):
     torch.cuda.synchronize()
     ids = v.topk_ids.cpu().numpy()
     w = v.topk_w.cpu().numpy().astype(np.float64)
-    check_dispatch(v.disp.arrays(), O.dispatch(ids, wl.E, 0, q.tile_rows), wl.E)
-    toks = sorted({0, wl.T // 2, wl.T - 1})
-    ref = O.forward_tokens(inp.x, *_fp8(winp), wl.dtype, ids, w, toks)
-    err = float(np.abs(host64(out)[toks] - ref).max() / np.abs(ref).max())
-    print(f"[gpu fp8 fullsize] {name}: tokens {toks} rel err {err:.3e}, tile rows {q.tile_rows}")
+    differ = check_routing(ids, w, O.router_logits(inp.x, inp.wr, wl.dtype), wl.k)
+    assert differ <= max(1, wl.T // 200), differ
+    ref_disp = O.dispatch(ids, wl.E, 0, q.tile_rows)
+    check_dispatch(v.disp.arrays(), ref_disp, wl.E)
+    ow = _fp8(winp)
+    e = int(np.argmax(ref_disp["counts"]))
+    rows, h_ref, y_ref = O.expert_rows(inp.x, *ow, wl.dtype, ref_disp, e)
+    idx = torch.from_numpy(rows).cuda()
+    eh, ey = rel_err(host64(v.h[idx]), h_ref), rel_err(host64(v.y_perm[idx]), y_ref)
+    print(f"[gpu fp8 fullsize] {name}: expert {e}, {rows.size} rows: h rel err {eh:.3e}, y_perm {ey:.3e}",
+          flush=True)
+    assert eh <= TOL["bf16"] and ey <= TOL["bf16"], (eh, ey)
+    ref = O.forward(inp.x, inp.wr, *ow, wl.k, wl.dtype, topk_ids=ids, topk_w=w)["out"]
+    err = rel_err(host64(out), ref)
+    print(f"[gpu fp8 fullsize] {name}: all {wl.T} tokens rel err {err:.3e}, tile rows {q.tile_rows}", flush=True)
     assert err <= TOL["bf16"]

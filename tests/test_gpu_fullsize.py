@@ -1,24 +1,23 @@
 """GPU parity at the workloads' full sizes, through moe_forward (the call the
 benchmark times).
 
-The oracle cannot run whole layers of this size in seconds, so:
   * routing (when the router runs) is checked for every token against the
     oracle's float64 logits (ids exact up to near-ties, weights to 2e-6);
   * every integer dispatch output is checked bit-exactly for every entry;
-  * the layer output is checked on sampled tokens (first, middle, last, and
-    in capacity mode tokens that went through the overflow region) against
-    the oracle's per-token evaluation with the GPU's routing;
+  * the layer output is checked for every token against the oracle's whole
+    layer run on the GPU's routing (max|gpu - oracle| / max|oracle|);
+  * the SwiGLU intermediate h and the expert output y_perm are checked on
+    every live row of the expert with the most rows (in capacity mode: the
+    expert with the most overflow rows, so both regions are covered);
   * capacity mode must give the uncapped output (bitwise with the same tile
     configuration).
 """
-import dataclasses
-
 import numpy as np
 import pytest
 
 from oracle import moe_oracle as O
-from tests.gpu_helpers import TOL, bits, check_dispatch, check_routing, dev, host64, torch_dtype
-from workloads import WORKLOADS, get_workload, make_inputs
+from tests.gpu_helpers import TOL, bits, check_dispatch, check_routing, dev, host64, rel_err, torch_dtype
+from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -68,6 +67,20 @@ def _run(wl, inp, devw, capacity=None, tile_rows=0):
     return q, v, out
 
 
+def check_expert_rows(name, x, host_w, dtype, ref_disp, v, capacity):
+    """h and y_perm on every live row of one expert against the oracle."""
+    counts = ref_disp["spill_counts"] if capacity else ref_disp["counts"]
+    e = int(np.argmax(counts))
+    rows, h_ref, y_ref = O.expert_rows(x, host_w[0], host_w[1], host_w[2], dtype, ref_disp, e)
+    h_gpu = host64(v.h[torch.from_numpy(rows).cuda()])
+    y_gpu = host64(v.y_perm[torch.from_numpy(rows).cuda()])
+    eh, ey = rel_err(h_gpu, h_ref), rel_err(y_gpu, y_ref)
+    print(f"[gpu fullsize] {name}: expert {e}, {rows.size} rows: h rel err {eh:.3e}, y_perm rel err {ey:.3e}",
+          flush=True)
+    assert rows.size > 0
+    assert eh <= TOL[dtype] and ey <= TOL[dtype], (eh, ey)
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_fullsize(weights, name):
     wl = WORKLOADS[name]
@@ -86,16 +99,15 @@ def test_fullsize(weights, name):
     ref_disp = O.dispatch(ids, wl.E, wl.capacity, q.tile_rows)
     check_dispatch(v.disp.arrays(), ref_disp, wl.E)
     assert ref_disp["kept_counts"].sum() + ref_disp["spill_counts"].sum() == wl.T * wl.k  # nothing dropped
-    # sampled tokens: ends, middle, and (capacity) tokens with a slot in the overflow region
-    toks = sorted({0, wl.T // 2, wl.T - 1})
     if wl.capacity:
-        spilled = np.nonzero((ref_disp["row_of"].reshape(wl.T, wl.k) >= wl.E * wl.capacity).any(axis=1))[0]
-        assert spilled.size > 0
-        toks = sorted(set(toks) | set(spilled[[0, spilled.size // 2, -1]].tolist()))
-    ref = O.forward_tokens(inp.x, host_w[0], host_w[1], host_w[2], wl.dtype, ids, w, toks)
-    got = host64(out)[toks]
-    err = float(np.abs(got - ref).max() / np.abs(ref).max())
-    print(f"[gpu fullsize] {name}: sampled tokens {toks} rel err {err:.3e}, tile rows {q.tile_rows}")
+        assert ref_disp["spill_counts"].sum() > 0
+    check_expert_rows(name, inp.x, host_w, wl.dtype, ref_disp, v, wl.capacity)
+    # every token: the oracle's whole layer on the GPU's routing
+    ref = O.forward(inp.x, inp.wr, host_w[0], host_w[1], host_w[2], wl.k, wl.dtype, topk_ids=ids, topk_w=w,
+                    capacity=wl.capacity)["out"]
+    got = host64(out)
+    err = rel_err(got, ref)
+    print(f"[gpu fullsize] {name}: all {wl.T} tokens rel err {err:.3e}, tile rows {q.tile_rows}", flush=True)
     assert err <= TOL[wl.dtype]
     if wl.capacity:
         # the overflow pass gives the uncapped layer output; with the same tile
