@@ -5,10 +5,15 @@
 A step is one whole layer (routing, count/scan, permutation, fused gate+up
 SwiGLU grouped GEMM, down grouped GEMM, combine) over one batch of seeded
 synthetic input, replayed from a hipGraph with every input already resident
-in HBM.  Prints one JSON line with tokens/s, the grouped-GEMM MFMA and HBM
-fractions, the roofline of the dominant kernel (the fused gate+up GEMM, timed
-with HIP events on the stream it runs on) and the CPU oracle's rate on a
-bounded sample of the same workload.
+in HBM.  Before the W warm-up replays the graph is replayed for --settle-ms
+of wall time (reported as `clock_settle`): the GPU raises its clocks over the
+first tens of milliseconds of load, and the requested warm-up alone may be
+too short for that.  The K timed replays each sit between two HIP events;
+`ms_per_step` is the median of those K single-replay times and `value` is T
+over it (tokens/s).  Prints one JSON line with that throughput, the
+grouped-GEMM MFMA and HBM fractions, the roofline of the dominant kernel
+(the fused gate+up GEMM, timed with HIP events on the stream it runs on) and
+the CPU oracle's rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -38,9 +43,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # the GPU raises its clocks over the first tens of milliseconds of load:
-    # the default warm-up (about 0.1 s of replays) reaches the steady state
     ap.add_argument("--warmup", type=int, default=150)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="wall time of graph replays run before the warm-up so the clocks reach their "
+                         "loaded level (reported as clock_settle; 0 disables)")
     ap.add_argument("--workload", default="mixtral_t512")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -399,6 +405,44 @@ def measured_peaks():
                       "512-2048 workgroups"}
 
 
+def host_cpu() -> dict:
+    """The host CPU the oracle runs on: model name, os.cpu_count(), the CPUs
+    this process may run on, and the CPU quota of its control group (None if
+    it sets none)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+            if q != "max":
+                quota = float(q) / float(period)
+    except (OSError, ValueError):
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"model": model, "os_cpu_count": os.cpu_count(), "affinity": affinity, "cgroup_cpu_quota": quota}
+
+
+def oracle_threads(cpu: dict) -> int:
+    """BLAS threads for the oracle: os.cpu_count(), unless the process may use
+    fewer CPUs (affinity mask or control-group quota), then that many."""
+    n = cpu["os_cpu_count"] or 1
+    n = min(n, cpu["affinity"])
+    if cpu["cgroup_cpu_quota"]:
+        n = min(n, max(1, int(cpu["cgroup_cpu_quota"])))
+    return n
+
+
 def cpu_baseline(wl, inp, sample_tokens):
     """The oracle as it stands on the workload (or its first `sample_tokens`
     tokens), repeated until about 12 s of CPU time have been spent."""
@@ -409,7 +453,8 @@ def cpu_baseline(wl, inp, sample_tokens):
     wg, wu, wd = inp.wg, inp.wu, inp.wd
     if wl.weights == "e4m3":
         wg, wu, wd = O.Fp8Weights(inp.wg, inp.sg), O.Fp8Weights(inp.wu, inp.su), O.Fp8Weights(inp.wd, inp.sd)
-    cores = min(16, os.cpu_count() or 1)
+    cpu = host_cpu()
+    cores = oracle_threads(cpu)
     reps, total = 0, 0.0
     with threadpool_limits(limits=cores):
         while reps == 0 or (total < 12.0 and reps < 10):
@@ -423,8 +468,10 @@ def cpu_baseline(wl, inp, sample_tokens):
             total += time.perf_counter() - t0
             reps += 1
     return {"value": n * reps / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu["model"], "os_cpu_count": cpu["os_cpu_count"], "cpu_affinity": cpu["affinity"],
+            "cgroup_cpu_quota": cpu["cgroup_cpu_quota"],
             "sample": f"{n} of {wl.T} tokens of {wl.name} (seed 0), whole layer in float64, "
-                      f"{reps} run(s), {total:.1f} s"}
+                      f"{reps} run(s), {total:.1f} s, {cores} BLAS threads"}
 
 
 def main():
@@ -516,20 +563,34 @@ def main():
     with torch.cuda.graph(g):
         step()
     torch.cuda.synchronize()
+    # clock settling: replays for --settle-ms of wall time, before the warm-up
+    settle_n, t_settle = 0, time.perf_counter()
+    while args.settle_ms > 0 and (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(20):
+            g.replay()
+        torch.cuda.synchronize()
+        settle_n += 20
+    settle = {"replays": settle_n, "ms": round((time.perf_counter() - t_settle) * 1e3, 1)}
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # the timed region: exactly K replays, each between two HIP events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    for a, b in evs:
+        a.record()
         g.replay()
-    e1.record()
+        b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"{args.steps} graph replays: {ms * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step)")
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    ms = float(np.median(per))
+    spread = {"p10": round(float(np.percentile(per, 10)), 4), "p50": round(ms, 4),
+              "p90": round(float(np.percentile(per, 90)), 4), "mean": round(float(per.mean()), 4),
+              "wall_mean": round(wall * 1e3 / args.steps, 4)}
+    log(f"clock settling: {settle['replays']} replays in {settle['ms']} ms; {args.steps} timed graph replays: "
+        f"median {ms * 1e3:.1f} us, mean {per.mean() * 1e3:.1f} us, wall {wall * 1e6 / args.steps:.1f} us per step")
 
     # per-call times (HIP events on the stream the kernels run on)
     cur = torch.cuda.current_stream()
@@ -572,18 +633,6 @@ def main():
         t_route = timed(lambda: M.moe_route(shape, x, wr, bias, rid, rw), it)
     log(f"per call (us): route {t_route:.1f} permute {t_perm:.1f} gate_up {t_gu:.1f} down {t_dn:.1f} "
         f"combine {t_comb:.1f}")
-    # spread: the same replays timed one by one (events around each replay)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:
-        a.record()
-        g.replay()
-        b.record()
-    torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) for a, b in evs])
-    spread = {"p10": round(float(np.percentile(per, 10)), 4), "p50": round(float(np.median(per)), 4),
-              "p90": round(float(np.percentile(per, 90)), 4)}
-
-
     peaks = None if args.no_peaks else measured_peaks()
 
     gu_flops, gu_bytes, dn_flops, dn_bytes, active = gemm_work(wl, counts, dt_bytes, spill_counts)
@@ -634,7 +683,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "ms_per_step_single_replays": spread,
+        "ms_per_step_stats": spread,
+        "clock_settle": settle,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -18,7 +18,7 @@ def test_bench_prints_one_json_line_with_the_contract_keys():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "10", "--warmup", "10", "--no-cpu-baseline",
-           "--kernel-iters", "5"]
+           "--kernel-iters", "5", "--settle-ms", "50"]
     print("\n[gpu bench] " + " ".join(cmd[1:]), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=110, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -31,6 +31,11 @@ def test_bench_prints_one_json_line_with_the_contract_keys():
     assert d["n_gpus"] == 1 and d["steps"] == 10 and d["warmup"] == 10 and d["dtype"] == "bf16"
     assert d["config"]["workload"] == "mixtral_t512"
     assert d["value"] > 0 and abs(d["value"] - 512 / (d["ms_per_step"] * 1e-3)) / d["value"] < 1e-3
+    # ms_per_step is the median of the K single-replay times; the clock-settling
+    # replays before the warm-up are reported on their own
+    st = d["ms_per_step_stats"]
+    assert st["p10"] <= d["ms_per_step"] == st["p50"] <= st["p90"]
+    assert d["clock_settle"]["replays"] > 0 and d["clock_settle"]["ms"] >= 50
     roof = d["roofline"]
     for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert key in roof, key
