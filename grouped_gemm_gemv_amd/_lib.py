@@ -30,7 +30,7 @@ STATUS = {
 }
 
 EXPORTED = [
-    "moe_status_string", "moe_query", "moe_dispatch_carve", "moe_route", "moe_permute",
+    "moe_status_string", "moe_query", "moe_workspace_size", "moe_dispatch_carve", "moe_route", "moe_permute",
     "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_grouped_ffn", "moe_combine",
     "moe_forward", "moe_ffn_gate_up_fp8", "moe_ffn_down_fp8", "moe_forward_fp8", "moe_pack_blocked16",
 ]
@@ -78,6 +78,7 @@ def _declare(lib):
     lib.moe_status_string.restype = ctypes.c_char_p
     sig = {
         "moe_query": [S, P(MoeSizes)],
+        "moe_workspace_size": [S, P(ctypes.c_size_t)],
         "moe_dispatch_carve": [S, c_ptr, ctypes.c_size_t, D],
         "moe_route": [S, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr],
         "moe_permute": [S, c_ptr, c_ptr, D, c_ptr, c_ptr, ctypes.c_size_t, c_ptr],

@@ -58,6 +58,13 @@ def query(shape: Shape) -> MoeSizes:
     return out
 
 
+def workspace_size(shape: Shape) -> int:
+    """Bytes of workspace moe_forward needs (moe_workspace_size)."""
+    n = ctypes.c_size_t()
+    check("moe_workspace_size", lib().moe_workspace_size(ctypes.byref(shape.c()), ctypes.byref(n)))
+    return n.value
+
+
 class Dispatch:
     """Device buffer holding one moe_dispatch_t's arrays, with tensor views."""
 

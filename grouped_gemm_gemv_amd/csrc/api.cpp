@@ -102,6 +102,17 @@ int64_t row_space(const moe_shape_t& s) {
 
 size_t elt_bytes(const moe_shape_t& s) { return s.dtype == MOE_BF16 ? 2 : 4; }
 
+// The GEMM kernels address their operands with 32-bit buffer offsets:
+//  * a workgroup's weight descriptor spans up to 256 rows, and its lanes'
+//    offsets up to 256 rows plus the K loop, so one weight or activation row
+//    (d or F elements) may take at most kMaxRowBytes;
+//  * with the gather folded into the gate+up loads, a lane's offset into x is
+//    token * row bytes + the K position, and padding rows of a tile read at
+//    kPadOffset (past the end of x, so they return zeros), plus the K
+//    position: x may take at most kPadOffset bytes.
+constexpr int64_t kMaxRowBytes = int64_t(1) << 20;
+constexpr int64_t kPadOffset = 0x7ff00000;
+
 moe_status_t validate(const moe_shape_t* s) {
   if (s == nullptr) return MOE_ERR_NULL_PTR;
   if (s->T < 1 || s->E < 1 || s->E > 256 || s->k < 1 || s->k > s->E || s->k > 64 || s->capacity < 0 ||
@@ -111,12 +122,20 @@ moe_status_t validate(const moe_shape_t* s) {
   if (s->tile_rows != 0 && !supported_tile_rows(s->tile_rows)) return MOE_ERR_UNSUPPORTED;
   if (s->weight_layout != MOE_LAYOUT_ROWS && s->weight_layout != MOE_LAYOUT_BLOCKED16) return MOE_ERR_INVALID_ARG;
   if (s->d % 64 != 0 || s->F % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t eb = s->dtype == MOE_BF16 ? 2 : 4;
+  if ((int64_t)s->d * eb > kMaxRowBytes || (int64_t)s->F * eb > kMaxRowBytes) return MOE_ERR_UNSUPPORTED;
   const int64_t Tk = (int64_t)s->T * s->k;
   if (Tk >= INT32_MAX) return MOE_ERR_INVALID_ARG;
   const int64_t R = row_space(*s);
   if (R >= INT32_MAX) return MOE_ERR_INVALID_ARG;
   if ((int64_t)s->E * s->capacity >= INT32_MAX) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
+}
+
+// The gate+up GEMM reads x through token_of (see kPadOffset).
+moe_status_t validate_gather(const moe_shape_t& s) {
+  const int64_t eb = s.dtype == MOE_BF16 ? 2 : 4;
+  return (int64_t)s.T * s.d * eb <= kPadOffset ? MOE_OK : MOE_ERR_UNSUPPORTED;
 }
 
 // Layout of the dispatch buffer (byte offsets from its base).
@@ -329,6 +348,7 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_rou
                           void* workspace, size_t ws_bytes, moe_forward_views_t* views_out, hipStream_t stream) {
   moe_status_t st = validate(s);
   if (st != MOE_OK) return st;
+  if ((st = validate_gather(*s)) != MOE_OK) return st;
   if (!x || !w_gate || !w_up || !w_down || !out || !workspace) return MOE_ERR_NULL_PTR;
   if ((topk_ids_in == nullptr) != (topk_w_in == nullptr)) return MOE_ERR_INVALID_ARG;
   if (topk_ids_in == nullptr && w_router == nullptr) return MOE_ERR_NULL_PTR;
@@ -397,6 +417,14 @@ moe_status_t moe_query(const moe_shape_t* s, moe_sizes_t* out) {
   return MOE_OK;
 }
 
+moe_status_t moe_workspace_size(const moe_shape_t* s, size_t* bytes) {
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr) return MOE_ERR_NULL_PTR;
+  *bytes = make_plan(*s).forward_ws;
+  return MOE_OK;
+}
+
 moe_status_t moe_dispatch_carve(const moe_shape_t* s, void* base, size_t bytes, moe_dispatch_t* disp) {
   moe_status_t st = validate(s);
   if (st != MOE_OK) return st;
@@ -442,6 +470,7 @@ moe_status_t moe_ffn_gate_up_gather(const moe_shape_t* s, const void* x, const v
                                     const moe_dispatch_t* disp, int pass, void* h, hipStream_t stream) {
   moe_status_t st = validate(s);
   if (st != MOE_OK) return st;
+  if ((st = validate_gather(*s)) != MOE_OK) return st;
   if (!x || !w_gate || !w_up || !h) return MOE_ERR_NULL_PTR;
   if (pass < 0 || pass > kBothPasses) return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(*s);
@@ -514,6 +543,7 @@ moe_status_t moe_ffn_gate_up_fp8(const moe_shape_t* s, const void* x, const uint
   moe_status_t st = validate(s);
   if (st != MOE_OK) return st;
   if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((st = validate_gather(*s)) != MOE_OK) return st;
   if (!x || !w_gate || !w_up || !s_gate || !s_up || !h) return MOE_ERR_NULL_PTR;
   if (pass < 0 || pass > kBothPasses) return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(*s);

@@ -33,8 +33,14 @@
  *  - Results are bitwise reproducible run to run on one device: no floating
  *    point atomics; every reduction has a fixed order.
  *
- * Shape limits: T >= 1; 1 <= k <= E <= 256; k <= 64; d and F multiples of
- * 64; T*k and every row-space index below 2^31.
+ * Shape limits: T >= 1; 1 <= k <= E <= 256; k <= 64; T*k and every
+ * row-space index below 2^31.  d and F must be multiples of 64 (the
+ * matrix-core K loop moves 128 bytes of K per step; MOE_ERR_UNSUPPORTED
+ * otherwise) and a row of d or F elements at most 1 MiB (MOE_ERR_UNSUPPORTED:
+ * the kernels address a workgroup's operands with 32-bit offsets).  The
+ * calls that read x through token_of (moe_forward, moe_forward_fp8,
+ * moe_ffn_gate_up_gather, moe_ffn_gate_up_fp8) also need x to be at most
+ * 0x7ff00000 bytes (T*d*element size), else MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -133,6 +139,13 @@ const char* moe_status_string(int status);
 /* Fill `out` (host) with the sizes for shape `s` (host).  Host arithmetic
  * only.  Errors: MOE_ERR_NULL_PTR, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED. */
 moe_status_t moe_query(const moe_shape_t* s, moe_sizes_t* out);
+
+/* Bytes of workspace moe_forward and moe_forward_fp8 need for shape `s`
+ * (host), written to *bytes (host): the dispatch arrays, the routing of the
+ * batch when it is computed, h [R,F] and y_perm [R,d].  The same value as
+ * moe_query's forward_ws_bytes.  Host arithmetic only.  Errors:
+ * MOE_ERR_NULL_PTR, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED (as moe_query). */
+moe_status_t moe_workspace_size(const moe_shape_t* s, size_t* bytes);
 
 /* Point the arrays of `disp` (host struct) into the device buffer `base` of
  * `bytes` bytes (>= moe_sizes_t.dispatch_bytes; 256-byte aligned).  Host

@@ -127,6 +127,58 @@ def test_query_rejects_bad_shapes(kw, code):
     assert st == code
 
 
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_workspace_size_is_the_forward_workspace(name):
+    wl = WORKLOADS[name]
+    s = _shape(wl.T, wl.d, wl.E, wl.k, wl.F, wl.capacity, 1 if wl.dtype == "bf16" else 0)
+    st, q = _query(s)
+    n = ctypes.c_size_t()
+    assert st == 0 and _lib.lib().moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert n.value == q.forward_ws_bytes
+
+
+def test_workspace_size_errors():
+    lib = _lib.lib()
+    n = ctypes.c_size_t(7)
+    assert lib.moe_workspace_size(None, ctypes.byref(n)) == 2
+    assert lib.moe_workspace_size(ctypes.byref(_shape()), None) == 2
+    assert lib.moe_workspace_size(ctypes.byref(_shape(T=0)), ctypes.byref(n)) == 1
+    assert lib.moe_workspace_size(ctypes.byref(_shape(d=100)), ctypes.byref(n)) == 4
+    assert n.value == 7  # untouched on error
+
+
+@pytest.mark.parametrize("kw", [dict(d=(1 << 19) + 64), dict(F=(1 << 19) + 64),
+                                dict(d=(1 << 18) + 64, dt=0), dict(F=(1 << 18) + 64, dt=0)])
+def test_rows_past_one_mib_are_unsupported(kw):
+    # a weight or activation row above 1 MiB would leave the kernels' 32-bit offsets
+    st, _ = _query(_shape(**kw))
+    assert st == 4
+    ok = {k: (v - 64 if k in ("d", "F") else v) for k, v in kw.items()}
+    st, _ = _query(_shape(**ok))
+    assert st == 0
+
+
+@pytest.mark.parametrize("T,d,dt,code", [
+    (262144, 4096, 0, 4),    # fp32 x of 4 GiB
+    (262144, 4096, 1, 4),    # bf16 x of 2 GiB
+    (262016, 4096, 1, 2),    # 0x7ff00000 bytes: accepted (then the null pointers are reported)
+])
+def test_x_past_the_gather_offset_range_is_unsupported(T, d, dt, code):
+    # moe_forward and the gather-folded gate+up address x with 32-bit offsets
+    lib = _lib.lib()
+    s = _shape(T=T, d=d, E=8, k=2, F=256, dt=dt)
+    st, q = _query(s)
+    assert st == 0
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_forward(ctypes.byref(s), None, fake, None, None, None, fake, fake, fake, fake, fake,
+                           1 << 62, None, None) == code
+    assert lib.moe_ffn_gate_up_gather(ctypes.byref(s), None, fake, fake, None, 0, fake, None) == code
+    if dt == 1:
+        assert lib.moe_forward_fp8(ctypes.byref(s), None, fake, None, None, None, fake, fake, fake, fake, fake,
+                                   fake, fake, fake, 1 << 62, None, None) == code
+        assert lib.moe_ffn_gate_up_fp8(ctypes.byref(s), None, fake, fake, fake, fake, None, 0, fake, None) == code
+
+
 def test_null_pointers_rejected_before_gpu():
     lib = _lib.lib()
     s = _shape()
