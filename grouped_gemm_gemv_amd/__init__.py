@@ -19,6 +19,7 @@ from .api import (
     moe_ffn_gate_up,
     moe_ffn_gate_up_gather,
     moe_forward,
+    moe_forward_noalloc,
     moe_grouped_ffn,
     moe_permute,
     moe_route,
@@ -28,7 +29,7 @@ from .api import (
 )
 
 __all__ = [
-    "Dispatch", "ForwardViews", "Shape", "moe_combine", "moe_ffn_down", "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_forward",
+    "Dispatch", "ForwardViews", "Shape", "moe_combine", "moe_ffn_down", "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_forward", "moe_forward_noalloc",
     "moe_ffn_gate_up_fp8", "moe_ffn_down_fp8", "moe_forward_fp8", "moe_pack_blocked16",
     "LAYOUT_ROWS", "LAYOUT_BLOCKED16", "PASS_BOTH",
     "moe_grouped_ffn", "moe_permute", "moe_route", "query", "workspace", "workspace_size",

@@ -19,6 +19,7 @@ c_ptr = ctypes.c_void_p
 
 MOE_F32 = 0
 MOE_BF16 = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 STATUS = {
     0: "MOE_OK",
@@ -33,6 +34,7 @@ EXPORTED = [
     "moe_status_string", "moe_query", "moe_workspace_size", "moe_dispatch_carve", "moe_route", "moe_permute",
     "moe_ffn_gate_up", "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_grouped_ffn", "moe_combine",
     "moe_forward", "moe_ffn_gate_up_fp8", "moe_ffn_down_fp8", "moe_forward_fp8", "moe_pack_blocked16",
+    "moe_forward_noalloc",
 ]
 
 
@@ -94,6 +96,8 @@ def _declare(lib):
         "moe_forward_fp8": [S, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                             c_ptr, c_ptr, ctypes.c_size_t, P(MoeForwardViews), c_ptr],
         "moe_pack_blocked16": [c_ptr, c_ptr, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, c_ptr],
+        "moe_forward_noalloc": [S, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
+                                P(MoeForwardViews), c_ptr],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -234,3 +234,15 @@ def moe_forward_fp8(shape: Shape, x, w_router, bias, topk_ids, topk_w, w_gate, w
         _p(w_down), _p(s_gate), _p(s_up), _p(s_down), _p(out), _p(ws), ws.numel(), ctypes.byref(v),
         _stream(stream)))
     return _forward_views(shape, v, ws, topk_ids, topk_w)
+
+
+def moe_forward_noalloc(shape: Shape, x, w_router, bias, topk_ids, topk_w, w_gate, w_up, w_down, out,
+                        stream=None) -> MoeForwardViews:
+    """The whole layer with the library's own device scratch array instead of a
+    workspace (for callers that cannot allocate); returns the raw views struct
+    (device addresses inside that array, valid until the next call)."""
+    v = MoeForwardViews()
+    check("moe_forward_noalloc", lib().moe_forward_noalloc(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(topk_ids), _p(topk_w), _p(w_gate), _p(w_up),
+        _p(w_down), _p(out), ctypes.byref(v), _stream(stream)))
+    return v

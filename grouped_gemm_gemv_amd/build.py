@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "libmoe.so")
 PEAKS_LIB = os.path.join(PKG, "libmoe_peaks.so")
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "gemm_bf16_gateup.hip", "gemm_bf16_down.hip",
-           "gemm_f32_gateup.hip", "gemm_f32_down.hip", "gemm_fp8w_gateup.hip", "gemm_fp8w_down.hip", "layout.hip"]
+           "gemm_f32_gateup.hip", "gemm_f32_down.hip", "gemm_fp8w_gateup.hip", "gemm_fp8w_down.hip", "layout.hip",
+           "noalloc.hip"]
 PEAKS_SOURCES = ["peaks.hip"]
 
 

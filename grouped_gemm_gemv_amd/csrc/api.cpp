@@ -523,6 +523,24 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
                       nullptr, out, workspace, ws_bytes, views_out, stream);
 }
 
+moe_status_t moe_forward_noalloc(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
+                                 const int32_t* topk_ids_in, const float* topk_w_in, const void* w_gate,
+                                 const void* w_up, const void* w_down, void* out, moe_forward_views_t* views_out,
+                                 hipStream_t stream) {
+  static_assert(moe::kNoallocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size");
+  moe_status_t st = validate(s);
+  if (st != MOE_OK) return st;
+  if (make_plan(*s).forward_ws > moe::kNoallocScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = validate_gather(*s)) != MOE_OK) return st;
+  if (!x || !w_gate || !w_up || !w_down || !out) return MOE_ERR_NULL_PTR;
+  if ((topk_ids_in == nullptr) != (topk_w_in == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (topk_ids_in == nullptr && w_router == nullptr) return MOE_ERR_NULL_PTR;
+  void* scratch = nullptr;
+  if (moe::noalloc_scratch(&scratch) != hipSuccess) return MOE_ERR_HIP;
+  return forward_impl(s, x, w_router, bias, topk_ids_in, topk_w_in, w_gate, w_up, w_down, nullptr, nullptr,
+                      nullptr, out, scratch, moe::kNoallocScratchBytes, views_out, stream);
+}
+
 moe_status_t moe_pack_blocked16(const void* src, void* dst, int64_t matrices, int64_t rows, int64_t row_bytes,
                                 hipStream_t stream) {
   if (!src || !dst) return MOE_ERR_NULL_PTR;

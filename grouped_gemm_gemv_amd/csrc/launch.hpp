@@ -90,6 +90,13 @@ struct GemmArgs {
   int blocked16;             // 1: weights in 16-row blocked order (moe_weight_layout_t)
 };
 
+// Bytes of the device scratch array of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+
+// Device address of that array on the current device, taken once per device
+// (hipGetSymbolAddress) and kept; never the array's host-side name.
+hipError_t noalloc_scratch(void** out);
+
 hipError_t launch_gemm_bf16_gateup(int BM, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_bf16_down(int BM, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_f32_gateup(int BM, const GemmArgs& a, hipStream_t stream);

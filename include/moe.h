@@ -242,6 +242,32 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
                          const void* w_up, const void* w_down, void* out, void* workspace,
                          size_t ws_bytes, moe_forward_views_t* views_out, hipStream_t stream);
 
+/* ---- a forward pass that allocates nothing --------------------------------
+ * For callers that cannot allocate device memory (code under hipGraph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * moe_forward with the workspace replaced by a device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library.  The caller still passes the
+ * inputs and the output; the arguments and results are those of moe_forward.
+ *  - Each GPU the library runs this on holds its own copy of the array (64
+ *    MiB) from the first call on it until the process ends; the first call on
+ *    a device takes the array's device address (hipGetSymbolAddress), later
+ *    calls reuse it.  No call allocates, frees or synchronises.
+ *  - Shapes whose moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *    return MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.
+ *  - Every call on one GPU shares that GPU's array and it keeps the last
+ *    call's contents (nothing in it needs to start zeroed: every kernel
+ *    writes what it later reads).  Calls that overlap on one GPU (other
+ *    streams, other threads) race on it and must be ordered by the caller.
+ *  - views_out, if not NULL, receives where the intermediates of this call
+ *    live inside the array (device pointers, valid until the next call).
+ *  - Unlike the other entry points this one keeps mutable global state: the
+ *    per-device addresses of the array (set once, under a lock). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_forward_noalloc(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
+                                 const int32_t* topk_ids_in, const float* topk_w_in, const void* w_gate,
+                                 const void* w_up, const void* w_down, void* out, moe_forward_views_t* views_out,
+                                 hipStream_t stream);
+
 /* Re-store `matrices` row-major matrices of `rows` rows of `row_bytes` bytes
  * each (src, contiguous) in MOE_LAYOUT_BLOCKED16 order (dst, same size, must
  * not overlap src; both 16-byte aligned).  A byte permutation: any element

@@ -179,6 +179,25 @@ def test_x_past_the_gather_offset_range_is_unsupported(T, d, dt, code):
         assert lib.moe_ffn_gate_up_fp8(ctypes.byref(s), None, fake, fake, fake, fake, None, 0, fake, None) == code
 
 
+def test_noalloc_size_and_argument_checks_return_before_any_hip_call():
+    # the scratch size check and the argument checks come before the first
+    # HIP call (taking the scratch array's device address)
+    lib = _lib.lib()
+    fake = ctypes.c_void_p(0x1000)
+    big = _shape(T=512, d=4096, E=8, k=2, F=28672)
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0 and n.value > _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(big), fake, fake, None, None, None, fake, fake, fake, fake,
+                                   None, None) == 3
+    s = _shape()
+    assert lib.moe_forward_noalloc(ctypes.byref(s), None, fake, None, None, None, fake, fake, fake, fake,
+                                   None, None) == 2
+    assert lib.moe_forward_noalloc(ctypes.byref(s), fake, fake, None, fake, None, fake, fake, fake, fake,
+                                   None, None) == 1
+    assert lib.moe_forward_noalloc(ctypes.byref(_shape(T=0)), fake, fake, None, None, None, fake, fake, fake,
+                                   fake, None, None) == 1
+
+
 def test_null_pointers_rejected_before_gpu():
     lib = _lib.lib()
     s = _shape()
