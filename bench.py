@@ -95,7 +95,9 @@ def gemm_source_hash() -> str:
 
 def gemm_role(kernel_name: str):
     """'gateup' or 'down' for a grouped-GEMM kernel name (its sixth template
-    argument is the gated flag), else None."""
+    argument is the gated flag; the two-width kernel is gate+up only), else None."""
+    if "grouped_gemm_wide_kernel<" in kernel_name:
+        return "gateup"
     key = "grouped_gemm_kernel<"
     if key not in kernel_name:
         return None
@@ -602,17 +604,22 @@ def main():
     wts = views.topk_w
 
     def timed(fn, iters):
-        for _ in range(10):
+        """Mean duration of one call of fn in microseconds, each call timed on
+        its own (two HIP events on the stream it runs on) right after a graph
+        replay of the whole layer, so it runs in the clock and cache state of
+        the timed layer."""
+        for _ in range(3):
+            g.replay()
             fn()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
         cur.synchronize()
-        a.record(cur)
-        for _ in range(iters):
+        for a, b in evs:
+            g.replay()
+            a.record(cur)
             fn()
-        b.record(cur)
-        b.synchronize()
-        return a.elapsed_time(b) / iters * 1e3  # us
+            b.record(cur)
+        cur.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3  # us
 
     it = args.kernel_iters
     # the GEMM launches exactly as moe_forward runs them: the gather folded

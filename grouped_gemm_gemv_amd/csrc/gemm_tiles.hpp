@@ -62,6 +62,20 @@ template <> struct TileCfg<160, true, true> { using type = TileShape<160, 32, 8,
 // activation fragment read from LDS feeds four MFMAs (two at BM 192).
 template <> struct TileCfg<384, true> { using type = TileShape<128, 32, 8, 1, 2, 4, 3>; };
 
+// bf16 gate+up on the 160-row tile map, from about 48 rows per expert (one
+// launch of grouped_gemm_wide_kernel): tiles of at most 144 rows in 224-column
+// workgroups, 32 weight rows per wavefront, non-temporal weights for an
+// expert with a single tile; tiles past 144 rows (whose accumulators would not
+// fit in the registers at 32 weight rows per wavefront) in the 112-column
+// shape above.  Measured on the vector memory path of the compute units, the
+// shared limit here: each activation byte moved into LDS feeds twice the
+// weight bytes (Mixtral shape, 128 rows per expert: gate+up 321 vs 363 us;
+// at 32 rows per expert 2 % slower, hence the threshold).
+struct Wide160 {
+  using wide = TileShape<144, 32, 7, 1, 2, 9>;
+  using narrow = TileCfg<160, true>::type;
+};
+
 // down projection
 template <> struct TileCfg<16, false> { using type = TileShape<16, 16, 1, 4, 4, 1>; };
 template <> struct TileCfg<32, false> { using type = TileShape<32, 32, 1, 4, 4, 2>; };

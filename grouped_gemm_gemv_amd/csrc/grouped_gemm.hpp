@@ -106,6 +106,8 @@ template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTM
 struct Gemm {
   using Elt = typename Tr::T;
   static_assert(!WQ || std::is_same<Tr, TBF16>::value, "fp8 weights take bf16 activations");
+  static constexpr bool WQ_ = WQ;
+  static constexpr int WTN_ = WTN, WN_ = WN, WK_ = WK;
   static constexpr int NTH = 64 * WN * WK;
   static constexpr int NSUB = WTN / 16;
   static constexpr int NMAT = GATED ? 2 : 1;
@@ -431,6 +433,58 @@ struct Gemm {
   }
 };
 
+// Fill the context of one workgroup of Gemm G: expert e, tile rows
+// [row0, row0 + rows), weight rows [nbase, nbase + G::BN) of each projection;
+// `stages` are the workgroup's LDS stage arrays.
+template <class G>
+__device__ __forceinline__ void setup_ctx(typename G::Ctx& c, const GemmArgs& p, char* const* stages, int e,
+                                          int row0, int rows, int nbase, int wave, int lane) {
+  using Elt = typename G::Elt;
+  constexpr bool WQ = G::WQ_;
+  const int ld = p.K * (int)sizeof(Elt);
+  c.ld = ld;
+  c.ldo = (size_t)p.N * sizeof(Elt);
+  c.nk = ld / kKB;
+  c.nit = (c.nk + G::WK_ - 1) / G::WK_;
+  c.rows = rows;
+  c.N = p.N;
+  c.wk = wave / G::WN_;
+  c.n0 = nbase + (wave % G::WN_) * G::WTN_;
+  c.out = reinterpret_cast<char*>(p.out) + (size_t)row0 * c.ldo;
+#pragma unroll
+  for (int i = 0; i < G::NA; ++i) c.stage[i] = stages[i];
+  if (p.act_rows != nullptr) {
+    // activation row r of the tile is row act_rows[row0 + r] of the source
+    c.arow = p.act_rows + row0;
+    c.act = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.act), (short)0, p.act_nrows * ld, 0x00020000);
+  } else {
+    c.arow = nullptr;
+    c.act = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(p.act) + (size_t)row0 * ld), (short)0, rows * ld, 0x00020000);
+  }
+  const int ldw = WQ ? p.K : ld;               // weight row bytes (one byte per fp8 code)
+  const size_t wbase = (size_t)e * p.N * ldw + (size_t)nbase * ldw;
+  const int wbytes = min(G::BN, p.N - nbase) * ldw;  // reads past N return 0 (column tail)
+  c.w[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(reinterpret_cast<const char*>(p.w0) + wbase),
+                                             (short)0, wbytes, 0x00020000);
+  if (G::NMAT == 2)
+    c.w[G::NMAT - 1] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(p.w1) + wbase), (short)0, wbytes, 0x00020000);
+  // row-major: lane reads row (lane % 16) of the subtile, 16 bytes at
+  // 16 (lane / 16) of each 64-byte half step.  Blocked 16-row order: the
+  // same bytes sit at row * 64 inside the 1024-byte block of that half step.
+  const int rowpitch = p.blocked16 ? 64 : ldw;
+  c.wstep = p.blocked16 ? 16 * G::KWB : G::KWB;
+  c.whalf = p.blocked16 ? 1024 : 64;
+#pragma unroll
+  for (int i = 0; i < G::NSUB; ++i)
+    c.wlane[i] = ((wave % G::WN_) * G::WTN_ + 16 * i) * ldw + (lane & 15) * rowpitch + (lane >> 4) * 16;
+  if constexpr (WQ) {
+    c.scale[0] = p.s0 + (size_t)e * p.N;
+    c.scale[G::NMAT - 1] = (G::NMAT == 2 ? p.s1 : p.s0) + (size_t)e * p.N;
+  }
+}
+
 template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int RS, int WS>
 __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) {
   using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, NTMS, WQ, WS>;
@@ -444,7 +498,10 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   __shared__ __attribute__((aligned(16))) char st6[G::NA > 6 ? G::STAGE : 16];
   __shared__ __attribute__((aligned(16))) char st7[G::NA > 7 ? G::STAGE : 16];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // uniform in the wavefront; saying so keeps the values derived from it (the
+  // K-split index, the weight rows' base) in scalar registers, so the weight
+  // loads take their K offset as a scalar operand
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // ---- which (expert, row tile, piece of it, column tile) this workgroup computes
   // (with a second pass merged in, an expert's tiles are its first-pass tiles
@@ -505,56 +562,144 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   const int rows = min(BM, ent.z - piece * BM);  // rows of this piece
   if (rows <= 0) return;
 
-  using Elt = typename G::Elt;
   typename G::Ctx c;
-  const int ld = p.K * (int)sizeof(Elt);
-  c.ld = ld;
-  c.ldo = (size_t)p.N * sizeof(Elt);
-  c.nk = ld / kKB;
-  c.nit = (c.nk + WK - 1) / WK;
-  c.rows = rows;
-  c.N = p.N;
-  c.wk = wave / WN;
-  const int nbase = nt * G::BN;               // first weight row of the workgroup
-  c.n0 = nbase + (wave % WN) * WTN;
-  c.out = reinterpret_cast<char*>(p.out) + (size_t)row0 * c.ldo;
   {
     char* const all[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
-#pragma unroll
-    for (int i = 0; i < G::NA; ++i) c.stage[i] = all[i];
-  }
-  if (p.act_rows != nullptr) {
-    // activation row r of the tile is row act_rows[row0 + r] of the source
-    c.arow = p.act_rows + row0;
-    c.act = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.act), (short)0, p.act_nrows * ld, 0x00020000);
-  } else {
-    c.arow = nullptr;
-    c.act = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(reinterpret_cast<const char*>(p.act) + (size_t)row0 * ld), (short)0, rows * ld, 0x00020000);
-  }
-  const int ldw = WQ ? p.K : ld;               // weight row bytes (one byte per fp8 code)
-  const size_t wbase = (size_t)e * p.N * ldw + (size_t)nbase * ldw;
-  const int wbytes = min(G::BN, p.N - nbase) * ldw;  // reads past N return 0 (column tail)
-  c.w[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(reinterpret_cast<const char*>(p.w0) + wbase),
-                                             (short)0, wbytes, 0x00020000);
-  if (GATED)
-    c.w[G::NMAT - 1] = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(reinterpret_cast<const char*>(p.w1) + wbase), (short)0, wbytes, 0x00020000);
-  // row-major: lane reads row (lane % 16) of the subtile, 16 bytes at
-  // 16 (lane / 16) of each 64-byte half step.  Blocked 16-row order: the
-  // same bytes sit at row * 64 inside the 1024-byte block of that half step.
-  const int rowpitch = p.blocked16 ? 64 : ldw;
-  c.wstep = p.blocked16 ? 16 * G::KWB : G::KWB;
-  c.whalf = p.blocked16 ? 1024 : 64;
-#pragma unroll
-  for (int i = 0; i < G::NSUB; ++i)
-    c.wlane[i] = ((wave % WN) * WTN + 16 * i) * ldw + (lane & 15) * rowpitch + (lane >> 4) * 16;
-  if constexpr (WQ) {
-    c.scale[0] = p.s0 + (size_t)e * p.N;
-    c.scale[G::NMAT - 1] = (GATED ? p.s1 : p.s0) + (size_t)e * p.N;
+    setup_ctx<G>(c, p, all, e, row0, rows, nt * G::BN, wave, lane);
   }
   // the weights are read by this workgroup alone if the expert's rows all fit in it
   G::template run_ms<G::MSUB>((rows + 15) >> 4, mt == 1 && ent.z <= BM, c);
+}
+
+// Fused gate+up over one pass of a tile map, with two column widths in one
+// launch.  CN is the configuration of the map's tile height (WTN weight rows
+// per wavefront); CW covers twice the columns per workgroup with the same
+// wavefronts (twice the weight rows each), so every activation tile loaded
+// into LDS feeds twice the weight bytes, but its accumulators fit in the
+// registers only for tiles of at most CW::BM rows.  Each tile of at most
+// CW::BM rows (in a map of CN::BM-row tiles only an expert's last tile can be
+// one) is worked in units of CW's width; the other tiles (more than CW::BM
+// rows) in units of CN's width.  Units are ordered expert-major, then by
+// column group of CW's width, so the units that read one slice of an
+// expert's weights stay consecutive: in column group g, the expert's
+// CW-width unit (if its last tile is short) and then its full tiles at the
+// CN-width columns 2g and 2g + 1.
+template <class Tr, class CW, class CN>
+__global__ __launch_bounds__(64 * CN::WN) void grouped_gemm_wide_kernel(GemmArgs p) {
+  using GW = Gemm<Tr, CW::BM, CW::WTN, CW::WN, 1, true, CW::PF, CW::NTMS, false, CW::WS>;
+  using GN = Gemm<Tr, CN::BM, CN::WTN, CN::WN, 1, true, CN::PF, CN::NTMS, false, CN::WS>;
+  static_assert(CW::WN == CN::WN && CW::WK == 1 && CN::WK == 1 && CW::RS == 1 && CN::RS == 1, "wide pair");
+  static_assert(CW::BM < CN::BM && CN::BM <= 2 * CW::BM && GW::BN == 2 * GN::BN, "wide pair");
+  constexpr int STAGE = GW::STAGE > GN::STAGE ? GW::STAGE : GN::STAGE;
+  constexpr int NA = GW::NA > GN::NA ? GW::NA : GN::NA;
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[STAGE];
+  __shared__ __attribute__((aligned(16))) char st3[NA > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st4[NA > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st5[NA > 5 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st6[NA > 6 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st7[NA > 7 ? STAGE : 16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NTw = (p.N + GW::BN - 1) / GW::BN;
+  const int NTn = (p.N + GN::BN - 1) / GN::BN;
+  const int4* map = reinterpret_cast<const int4*>(p.tile_map);
+  // units of expert i: its last tile in CW's width if it has at most CW::BM rows
+  auto units_of = [&](int i) {
+    const int t0 = p.tile_off[i], t1 = p.tile_off[i + 1];
+    if (t1 == t0) return 0;
+    const int sm = map[t1 - 1].z <= CW::BM ? 1 : 0;
+    return sm * NTw + (t1 - t0 - sm) * NTn;
+  };
+  // per 64-expert chunk: units of each expert, their total and the skew test's
+  // tile statistics (as in grouped_gemm_kernel)
+  int total = 0, mx = 0, act = 0;
+  for (int b = 0; b < p.E; b += 64) {
+    const int i = b + lane;
+    const int u = i < p.E ? units_of(i) : 0;
+    const int t = i < p.E ? p.tile_off[i + 1] - p.tile_off[i] : 0;
+    int su = u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) su += __shfl_xor(su, o);
+    total += su;
+    mx = max(mx, t);
+    act += __popcll(__ballot(t > 0));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+  total = __builtin_amdgcn_readfirstlane(total);
+  mx = __builtin_amdgcn_readfirstlane(mx);
+  const bool skewed = p.skew_map && (long long)mx * act > 2LL * p.n_tiles[0];
+  const int j = blockIdx.x >> 3;
+  int L;
+  if (!skewed) {
+    const int J = (total + 7) >> 3;
+    if (j >= J) return;
+    L = (blockIdx.x & 7) * J + j;
+  } else {
+    L = ((j / kXcdChunk) * 8 + (blockIdx.x & 7)) * kXcdChunk + j % kXcdChunk;
+  }
+  if (L >= total) return;
+  // expert of unit L: the number of experts whose units all lie at or before L;
+  // `before`: the units of the experts ahead of it
+  int e = 0, before = 0, carry = 0;
+  for (int b = 0; b < p.E; b += 64) {
+    const int i = b + lane;
+    const int u = i < p.E ? units_of(i) : 0;
+    int inc = u;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(inc, o);
+      if (lane >= o) inc += n;
+    }
+    const bool done = i < p.E && carry + inc <= L;
+    e += __popcll(__ballot(done));
+    int bu = done ? u : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) bu += __shfl_xor(bu, o);
+    before += bu;
+    carry += __shfl(inc, 63);
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  before = __builtin_amdgcn_readfirstlane(before);
+  const int t0 = p.tile_off[e];
+  const int mt = p.tile_off[e + 1] - t0;
+  const int sm = map[t0 + mt - 1].z <= CW::BM ? 1 : 0;  // short last tile
+  const int big = mt - sm;
+  const int local = L - before;
+  const int cw = local / (sm + 2 * big);                 // column group
+  const int slot = local - cw * (sm + 2 * big);
+  char* const stages[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
+  if (slot < sm) {
+    const int4 ent = map[t0 + mt - 1];
+    typename GW::Ctx c;
+    setup_ctx<GW>(c, p, stages, e, ent.y, ent.z, cw * GW::BN, wave, lane);
+    GW::template run_ms<GW::MSUB>((ent.z + 15) >> 4, mt == 1, c);
+  } else {
+    const int s2 = slot - sm;
+    const int cn = 2 * cw + s2 / big;  // CN-width column
+    const int4 ent = map[t0 + s2 % big];
+    typename GN::Ctx c;
+    setup_ctx<GN>(c, p, stages, e, ent.y, ent.z, cn * GN::BN, wave, lane);
+    // a tile of more than CW::BM rows has all of CN's subtiles (the constant
+    // count leaves only that main loop after inlining)
+    GN::template run_ms<GN::MSUB>(GN::MSUB, mt == 1, c);
+  }
+}
+
+template <class Tr, class Pair>
+hipError_t launch_wide(const GemmArgs& a, hipStream_t stream) {
+  using CN = typename Pair::narrow;
+  constexpr int BNn = CN::WN * CN::WTN;
+  const int NTn = (a.N + BNn - 1) / BNn;
+  const long long units = (long long)a.max_tiles * NTn;  // every tile in CN's width at most
+  const long long round = a.skew_map ? 8LL * kXcdChunk : 8;
+  const long long grid = ((units + round - 1) / round) * round;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_wide_kernel<Tr, typename Pair::wide, CN>), dim3((unsigned)grid),
+                     dim3(64 * CN::WN), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <class Tr, class Cfg, bool GATED, bool WQ>
@@ -573,6 +718,9 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 
 template <class Tr, bool GATED, bool WQ = false>
 hipError_t dispatch_bm(int BM, const GemmArgs& a, hipStream_t stream) {
+  if constexpr (GATED && !WQ && std::is_same<Tr, TBF16>::value) {
+    if (BM == 160 && a.wide && a.tile_off2 == nullptr) return launch_wide<Tr, Wide160>(a, stream);
+  }
   switch (BM) {
 #define MOE_BM_CASE(bm) \
   case bm:              \

@@ -88,6 +88,7 @@ struct GemmArgs {
   int max_tiles;             // tiles of the map(s) the grid must cover
   int skew_map;              // 1: uneven tile counts per expert deal chunks of units to the XCDs in turn
   int blocked16;             // 1: weights in 16-row blocked order (moe_weight_layout_t)
+  int wide;                  // 1: bf16 gate+up on the 160-row map may take the two-width kernel (one pass)
 };
 
 // Bytes of the device scratch array of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES).

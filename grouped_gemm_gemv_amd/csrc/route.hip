@@ -41,7 +41,9 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(const typename Tr::T* __
   __shared__ float logit[kTok][E16];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // uniform in the wavefront; saying so keeps the slab index, and with it the
+  // loads' K offset, in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * kTok;
   const int ntok = min(kTok, T - t0);
   const int row_bytes = d * (int)sizeof(Elt);

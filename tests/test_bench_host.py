@@ -16,6 +16,9 @@ def test_gemm_role_reads_the_gated_argument():
         for rs in (1, 2, 3):           # pieces per tile
             assert bench.gemm_role(GATE.format(wq=wq, rs=rs)) == "gateup"
             assert bench.gemm_role(DOWN.format(wq=wq, rs=rs)) == "down"
+    wide = ("void moe::gemm::grouped_gemm_wide_kernel<moe::TBF16, moe::TileShape<144, 32, 7, 1, 2, 9, 1, 0>, "
+            "moe::TileShape<160, 16, 7, 1, 4, 4, 1, 0> >(moe::GemmArgs)")
+    assert bench.gemm_role(wide) == "gateup"
     f32 = "void moe::gemm::grouped_gemm_kernel<moe::TF32, 16, 16, 1, 4, false, 4, 1, false, 1>(moe::GemmArgs)"
     assert bench.gemm_role(f32) == "down"
     for other in ("moe::(anonymous namespace)::dispatch_small_kernel(moe::SmallDispatchArgs)",
