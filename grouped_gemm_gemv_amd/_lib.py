@@ -19,7 +19,7 @@ c_ptr = ctypes.c_void_p
 
 MOE_F32 = 0
 MOE_BF16 = 1
-NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 STATUS = {
     0: "MOE_OK",
@@ -50,7 +50,7 @@ class MoeSizes(ctypes.Structure):
 
 
 DISPATCH_ARRAYS = ["counts", "offsets", "spill_counts", "spill_offsets", "row_of", "token_of",
-                   "tile_off", "tile_map", "n_tiles", "err_flags"]
+                   "tile_off", "tile_map", "n_tiles", "err_flags", "kpart"]
 
 
 class MoeDispatch(ctypes.Structure):

@@ -76,6 +76,25 @@ int choose_tile_rows(const moe_shape_t& s) {
   return (mean * 5 + 3) / 4 <= 16 ? 16 : 32;
 }
 
+int64_t mean_rows(const moe_shape_t& s) {
+  const int64_t Tk = (int64_t)s.T * s.k;
+  int64_t mean = ceil_div(Tk, std::min<int64_t>(s.E, Tk));
+  if (s.capacity > 0) mean = std::min<int64_t>(mean, s.capacity);
+  return mean;
+}
+
+// The bf16 down GEMM on the 160-row tile map splits its K loop in two
+// (Split160 in gemm_tiles.hpp) from this many mean rows per expert, where the
+// activation bytes moved into LDS weigh about as much as the weight bytes.
+// Measured, 8 Mixtral experts, down GEMM with the kernel adding the two
+// halves: 64 rows 152 vs 143 us, 96 rows 155 vs 162, 128 rows 164 vs 179,
+// 144 rows 168 vs 191.
+constexpr int kSplitMinRows = 80;
+
+bool split_down(const moe_shape_t& s, int BM) {
+  return BM == 160 && s.dtype == MOE_BF16 && mean_rows(s) >= kSplitMinRows && (int64_t)s.F * 2 >= 256;
+}
+
 int64_t spill_bound(const moe_shape_t& s) { return std::max<int64_t>(0, (int64_t)s.T * s.k - s.capacity); }
 
 // Upper bound on the tiles of one pass: a pass of R_p rows over at most E_p
@@ -141,12 +160,14 @@ moe_status_t validate_gather(const moe_shape_t& s) {
 // Layout of the dispatch buffer (byte offsets from its base).
 struct DispatchLayout {
   size_t counts, offsets, spill_counts, spill_offsets, row_of, token_of, tile_off, tile_map, n_tiles, err_flags;
+  size_t kpart;
   size_t bytes;
 };
 
 struct Plan {
   int64_t Tk, R;
   int BM;
+  bool ksplit;            // the bf16 down GEMM splits K in two (Split160): [2][R][d] fp32 partial sums
   int64_t max_tiles;      // stride of each pass in tile_map
   int64_t pass_tiles[2];  // grid bound of each pass
   int nblk;
@@ -163,6 +184,7 @@ Plan make_plan(const moe_shape_t& s) {
   p.pass_tiles[0] = pass_max_tiles(s, p.BM, 0);
   p.pass_tiles[1] = pass_max_tiles(s, p.BM, 1);
   p.max_tiles = std::max<int64_t>(1, std::max(p.pass_tiles[0], p.pass_tiles[1]));
+  p.ksplit = split_down(s, p.BM);
   p.nblk = (int)ceil_div(p.Tk, moe::kCountChunk);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -181,6 +203,7 @@ Plan make_plan(const moe_shape_t& s) {
   p.dl.tile_map = take(4 * 4 * 2 * (size_t)p.max_tiles);
   p.dl.n_tiles = take(4 * 2);
   p.dl.err_flags = take(4);
+  p.dl.kpart = take(p.ksplit ? 4 * 2 * (size_t)p.R * s.d : 0);
   p.dl.bytes = o;
   p.permute_ws = align_up(4 * (size_t)p.nblk * E) + align_up(4 * (size_t)p.nblk);
   const size_t eb = elt_bytes(s);
@@ -206,6 +229,7 @@ void carve(const moe_shape_t& s, const Plan& p, char* base, moe_dispatch_t* d) {
   d->tile_map = reinterpret_cast<int32_t*>(base + p.dl.tile_map);
   d->n_tiles = reinterpret_cast<int32_t*>(base + p.dl.n_tiles);
   d->err_flags = reinterpret_cast<uint32_t*>(base + p.dl.err_flags);
+  d->kpart = p.ksplit ? reinterpret_cast<float*>(base + p.dl.kpart) : nullptr;
   d->tile_rows = p.BM;
   d->max_tiles = (int32_t)p.max_tiles;
   (void)s;
@@ -216,6 +240,7 @@ moe_status_t check_dispatch(const moe_shape_t& s, const Plan& p, const moe_dispa
   if (!d->counts || !d->offsets || !d->spill_counts || !d->spill_offsets || !d->row_of || !d->token_of ||
       !d->tile_off || !d->tile_map || !d->n_tiles || !d->err_flags)
     return MOE_ERR_NULL_PTR;
+  if (split_down(s, d->tile_rows) && d->kpart == nullptr) return MOE_ERR_NULL_PTR;
   if (!supported_tile_rows(d->tile_rows)) return MOE_ERR_UNSUPPORTED;
   const int64_t need = std::max(pass_max_tiles(s, d->tile_rows, 0), pass_max_tiles(s, d->tile_rows, 1));
   if (d->max_tiles < need || d->max_tiles < 1) return MOE_ERR_INVALID_ARG;
@@ -310,6 +335,8 @@ moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass,
   a.skew_map = 1;
   a.blocked16 = s.weight_layout == MOE_LAYOUT_BLOCKED16 ? 1 : 0;
   a.wide = 0;
+  a.kpart = nullptr;
+  a.kplane = 0;
   return a;
 }
 
@@ -321,12 +348,6 @@ moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass,
 constexpr int kWideMinRows = 48;
 constexpr int kWideMaxRows = 136;
 
-int64_t mean_rows(const moe_shape_t& s) {
-  const int64_t Tk = (int64_t)s.T * s.k;
-  int64_t mean = ceil_div(Tk, std::min<int64_t>(s.E, Tk));
-  if (s.capacity > 0) mean = std::min<int64_t>(mean, s.capacity);
-  return mean;
-}
 
 // Gate+up over one pass.  With x_src set, activation row r is read from row
 // token_of[r] of x_src (the gather folded into the GEMM's loads); otherwise
@@ -352,11 +373,24 @@ moe_status_t enqueue_down(const moe_shape_t& s, const void* h, const void* wd, c
                           void* y, hipStream_t st, const float* sd = nullptr) {
   moe::GemmArgs a = gemm_args(s, d, pass, false);
   a.s0 = sd;
+  const bool split = sd == nullptr && split_down(s, d.tile_rows);
+  if (split) {
+    a.kpart = d.kpart;
+    a.kplane = (size_t)row_space(s) * s.d;
+  }
   a.act = h;
   a.w0 = wd;
   a.w1 = nullptr;
   a.out = y;
-  return hip_status(moe::launch_grouped_gemm(s.dtype, false, d.tile_rows, a, st));
+  moe_status_t st_ = hip_status(moe::launch_grouped_gemm(s.dtype, false, d.tile_rows, a, st));
+  if (st_ != MOE_OK || !split) return st_;
+  // y rows of the pass(es) just computed: the uncapped rows or the fixed
+  // region (pass 0), the overflow region (pass 1)
+  const int64_t fixed = s.capacity > 0 ? (int64_t)s.E * s.capacity : row_space(s);
+  const int64_t r0 = pass == 1 ? fixed : 0;
+  const int64_t r1 = (pass == 0 && s.capacity > 0) ? fixed : row_space(s);
+  return hip_status(moe::launch_k_split_finish(s.dtype, d.kpart + (size_t)r0 * s.d, a.kplane, d.token_of + r0, r1 - r0,
+                                                s.d, static_cast<char*>(y) + (size_t)r0 * s.d * elt_bytes(s), st));
 }
 
 // The whole layer; s_gate/s_up/s_down non-null: the weights are E4M3 codes.

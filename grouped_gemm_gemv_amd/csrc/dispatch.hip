@@ -262,6 +262,35 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const char* __restric
   }
 }
 
+// Sum of the two K ranges of the split down GEMM: one wavefront per row, fp32
+// planes added in plane order, one rounding to the element type.
+template <class Tr>
+__global__ __launch_bounds__(kThreads) void k_split_finish_kernel(const float* __restrict__ part, size_t plane,
+                                                                  const int32_t* __restrict__ token_of,
+                                                                  int64_t rows, int N, char* __restrict__ y) {
+  using Elt = typename Tr::T;
+  constexpr int EPC = Tr::EPC;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (r >= rows || token_of[r] < 0) return;
+  const float* p0 = part + (size_t)r * N;
+  const float* p1 = p0 + plane;
+  char* yr = y + (size_t)r * N * sizeof(Elt);
+  for (int c = lane * EPC; c < N; c += 64 * EPC) {
+    float v[EPC];
+#pragma unroll
+    for (int i = 0; i < EPC; i += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(p0 + c + i);
+      const float4 b = *reinterpret_cast<const float4*>(p1 + c + i);
+      v[i] = a.x + b.x;
+      v[i + 1] = a.y + b.y;
+      v[i + 2] = a.z + b.z;
+      v[i + 3] = a.w + b.w;
+    }
+    *reinterpret_cast<uint4*>(yr + (size_t)c * sizeof(Elt)) = narrow<Tr>(v);
+  }
+}
+
 // Whole dispatch (count, scans, capacity split, tile map, stable ranks) in
 // one workgroup of 1024 threads, for T*k up to kSmallDispatch: one launch
 // instead of three.  Same results as count + scan + scatter.
@@ -412,6 +441,18 @@ hipError_t launch_gather(const void* x, const int32_t* row_of, int Tk, int k, in
 
 hipError_t launch_dispatch_small(const SmallDispatchArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_k_split_finish(int dtype, const float* part, size_t plane, const int32_t* token_of, int64_t rows,
+                                 int N, void* y, hipStream_t stream) {
+  const dim3 grid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64))), block(kThreads);
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_split_finish_kernel<TBF16>, grid, block, 0, stream, part, plane, token_of, rows, N,
+                       static_cast<char*>(y));
+  else
+    hipLaunchKernelGGL(k_split_finish_kernel<TF32>, grid, block, 0, stream, part, plane, token_of, rows, N,
+                       static_cast<char*>(y));
   return hipGetLastError();
 }
 

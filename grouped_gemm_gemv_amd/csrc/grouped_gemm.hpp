@@ -102,7 +102,11 @@ __device__ __forceinline__ uint4 widen_e4m3(unsigned lo, unsigned hi) {
 
 // WQ: the weights are OCP E4M3 codes with one fp32 scale per output channel
 // (weight row); the activations stay bf16.
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int WS = 0>
+// KS: the K loop of every unit is split into KS consecutive ranges worked by
+// KS workgroups (KS = 1 or 2).  With KS = 2 each workgroup stores its fp32
+// partial sums, unrounded, in plane ks of a [2][R][N] buffer, and a separate
+// kernel adds the two planes (k_split_finish): no workgroup waits for another.
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int WS = 0, int KS = 1>
 struct Gemm {
   using Elt = typename Tr::T;
   static_assert(!WQ || std::is_same<Tr, TBF16>::value, "fp8 weights take bf16 activations");
@@ -124,6 +128,7 @@ struct Gemm {
   static constexpr int UNR = NWS == NA ? NA : NA * NWS;  // iterations per unrolled round
   static constexpr int STAGE = BM * ROWB;         // bytes per activation stage
   static_assert(WTN % 16 == 0 && BM % 16 == 0 && PF >= 2 && PF <= 7, "tile shape");
+  static_assert(KS == 1 || (KS == 2 && WK == 1 && !GATED), "K split");
 
   struct Ctx {
     __amdgpu_buffer_rsrc_t act;      // activation rows of the tile (reads past its rows return 0)
@@ -137,6 +142,7 @@ struct Gemm {
     size_t ldo;                      // output row bytes
     int ld;                          // activation/weight row bytes
     int nk, nit, rows, n0, N, wk;
+    int s0;                          // first K step of this workgroup's range (K split), else 0
   };
 
   // LDS swizzle of the activation tile: in row r, the 16-byte chunk c of each
@@ -202,7 +208,7 @@ struct Gemm {
     uint4 wq[NWS][WL];
 
     auto load_w = [&](int it, uint4* dst) {
-      const int s = min(it * WK + c.wk, c.nk - 1);  // clamped: values past the end are unused
+      const int s = c.s0 + min(it * WK + c.wk, c.nk - 1);  // clamped: values past the end are unused
       if constexpr (WQ) {
         // one 16-byte load holds this lane's codes of both K halves
 #pragma unroll
@@ -229,7 +235,8 @@ struct Gemm {
 #pragma unroll
       for (int i = 0; i < QW; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            c.act, (__attribute__((address_space(3))) void*)(st + lofs[i]), 16, aoff[i] + itc * ROWB, 0, 0, 0);
+            c.act, (__attribute__((address_space(3))) void*)(st + lofs[i]), 16, aoff[i] + itc * ROWB + c.s0 * kKB,
+            0, 0, 0);
     };
     // MFMA operands of one step, half h (32 of its 64 K elements).  bf16
     // weights: lane group g = lane/16 holds elements 32h + 8g .. +7 of both
@@ -334,6 +341,7 @@ struct Gemm {
     wait_vm<0>();
     __syncthreads();
 
+
     if constexpr (WK > 1) {
       // add the partial tiles of wk = 1, 2, ... into wk = 0, in that order
       constexpr int PART = NMAT * NSUB * MS * 4 * 64;  // floats per wavefront partial
@@ -405,7 +413,10 @@ struct Gemm {
             for (int r = 0; r < 4; ++r)
               v[r] = GATED ? silu_mul(acc[0][i][jm][r] * sc[0][i][r], acc[NMAT - 1][i][jm][r] * sc[NMAT - 1][i][r])
                            : acc[0][i][jm][r] * sc[0][i][r];
-            store4<Tr>(orow + (size_t)n * sizeof(Elt), v[0], v[1], v[2], v[3]);
+            if constexpr (KS == 2)
+              store4<TF32>(orow + (size_t)n * sizeof(float), v[0], v[1], v[2], v[3]);
+            else
+              store4<Tr>(orow + (size_t)n * sizeof(Elt), v[0], v[1], v[2], v[3]);
           }
         }
       }
@@ -446,6 +457,7 @@ __device__ __forceinline__ void setup_ctx(typename G::Ctx& c, const GemmArgs& p,
   c.ldo = (size_t)p.N * sizeof(Elt);
   c.nk = ld / kKB;
   c.nit = (c.nk + G::WK_ - 1) / G::WK_;
+  c.s0 = 0;
   c.rows = rows;
   c.N = p.N;
   c.wk = wave / G::WN_;
@@ -485,9 +497,9 @@ __device__ __forceinline__ void setup_ctx(typename G::Ctx& c, const GemmArgs& p,
   }
 }
 
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int RS, int WS>
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int RS, int WS, int KS>
 __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) {
-  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, NTMS, WQ, WS>;
+  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, NTMS, WQ, WS, KS>;
   // one LDS array per activation stage (stages past NA are 16-byte stubs)
   __shared__ __attribute__((aligned(16))) char st0[G::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[G::STAGE];
@@ -510,7 +522,7 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   auto tiles_before = [&](int i) { return p.tile_off[i] + (two ? p.tile_off2[i] : 0); };
   const int NT = (p.N + G::BN - 1) / G::BN;
   const int ntiles = p.n_tiles[0] + (two ? p.n_tiles2[0] : 0);
-  const int total = ntiles * NT * RS;
+  const int total = ntiles * NT * RS * KS;
   const int j = blockIdx.x >> 3;
   // Skew test, identical in every workgroup: are some experts' tile counts
   // well above the mean over active experts (max * active > 2 * tiles)?
@@ -539,6 +551,9 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
     L = ((j / kXcdChunk) * 8 + (blockIdx.x & 7)) * kXcdChunk + j % kXcdChunk;
   }
   if (L >= total) return;
+  // K split: the KS workgroups of a unit are consecutive in L
+  const int ks = L % KS;
+  L /= KS;
   // expert e owns units [tiles_before(e) * NT * RS, tiles_before(e+1) * NT * RS),
   // column tile major, then row tile, then piece
   int e = 0;
@@ -566,6 +581,16 @@ __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) 
   {
     char* const all[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
     setup_ctx<G>(c, p, all, e, row0, rows, nt * G::BN, wave, lane);
+  }
+  if constexpr (KS == 2) {
+    const int nk = c.nk;  // steps of the whole K loop: the first range takes the larger half
+    const int half = (nk + 1) / 2;
+    c.s0 = ks == 0 ? 0 : half;
+    c.nk = ks == 0 ? half : nk - half;
+    c.nit = c.nk;
+    // fp32 partial sums of range ks: plane ks of the [2][R][N] buffer
+    c.ldo = (size_t)p.N * sizeof(float);
+    c.out = reinterpret_cast<char*>(p.kpart + (size_t)ks * p.kplane) + (size_t)row0 * c.ldo;
   }
   // the weights are read by this workgroup alone if the expert's rows all fit in it
   G::template run_ms<G::MSUB>((rows + 15) >> 4, mt == 1 && ent.z <= BM, c);
@@ -702,16 +727,16 @@ hipError_t launch_wide(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class Tr, class Cfg, bool GATED, bool WQ>
+template <class Tr, class Cfg, bool GATED, bool WQ, int KS = 1>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   constexpr int BN = Cfg::WN * Cfg::WTN;
   const int NT = (a.N + BN - 1) / BN;
-  const long long units = (long long)a.max_tiles * NT * Cfg::RS;
+  const long long units = (long long)a.max_tiles * NT * Cfg::RS * KS;
   const long long round = a.skew_map ? 8LL * kXcdChunk : 8;  // chunked mapping: whole rounds of chunks
   const long long grid = ((units + round - 1) / round) * round;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::NTMS, WQ, Cfg::RS,
-                                         Cfg::WS>),
+                                         Cfg::WS, KS>),
                      dim3((unsigned)grid), dim3(64 * Cfg::WN * Cfg::WK), 0, stream, a);
   return hipGetLastError();
 }
@@ -720,6 +745,9 @@ template <class Tr, bool GATED, bool WQ = false>
 hipError_t dispatch_bm(int BM, const GemmArgs& a, hipStream_t stream) {
   if constexpr (GATED && !WQ && std::is_same<Tr, TBF16>::value) {
     if (BM == 160 && a.wide && a.tile_off2 == nullptr) return launch_wide<Tr, Wide160>(a, stream);
+  }
+  if constexpr (!GATED && !WQ && std::is_same<Tr, TBF16>::value) {
+    if (BM == 160 && a.kpart != nullptr) return launch_cfg<Tr, Split160, false, false, 2>(a, stream);
   }
   switch (BM) {
 #define MOE_BM_CASE(bm) \

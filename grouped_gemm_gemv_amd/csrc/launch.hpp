@@ -89,10 +89,18 @@ struct GemmArgs {
   int skew_map;              // 1: uneven tile counts per expert deal chunks of units to the XCDs in turn
   int blocked16;             // 1: weights in 16-row blocked order (moe_weight_layout_t)
   int wide;                  // 1: bf16 gate+up on the 160-row map may take the two-width kernel (one pass)
+  float* kpart;              // non-null: bf16 down on the 160-row map splits K in two; fp32 partial sums,
+                             // plane ks of [2][R][N] (kplane floats per plane)
+  size_t kplane;
 };
 
+// y[r] = rounded(part[0][r] + part[1][r]) for every row r with token_of[r] >= 0:
+// the sum of the two K ranges of the split down GEMM, added in that order.
+hipError_t launch_k_split_finish(int dtype, const float* part, size_t plane, const int32_t* token_of, int64_t rows,
+                                 int N, void* y, hipStream_t stream);
+
 // Bytes of the device scratch array of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES).
-constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+constexpr size_t kNoallocScratchBytes = size_t(128) << 20;
 
 // Device address of that array on the current device, taken once per device
 // (hipGetSymbolAddress) and kept; never the array's host-side name.

@@ -129,6 +129,9 @@ typedef struct moe_dispatch {
                               rows in tile (1..BM), tile index within expert}  */
   int32_t* n_tiles;        /* [2]      tiles in pass 0 and pass 1                */
   uint32_t* err_flags;     /* [1]      bit 0: an id outside [0, E) was skipped   */
+  float* kpart;            /* [2][R][d] fp32: the down GEMM's partial sums over the
+                              two halves of its K loop, when the shape splits it
+                              (bf16, 160-row tiles, >= 80 rows per expert), else NULL */
   int32_t tile_rows;       /* BM the tile map was built for                      */
   int32_t max_tiles;       /* entries reserved per pass in tile_map              */
 } moe_dispatch_t;
@@ -248,7 +251,7 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
  * moe_forward with the workspace replaced by a device array of
  * MOE_NOALLOC_SCRATCH_BYTES inside the library.  The caller still passes the
  * inputs and the output; the arguments and results are those of moe_forward.
- *  - Each GPU the library runs this on holds its own copy of the array (64
+ *  - Each GPU the library runs this on holds its own copy of the array (128
  *    MiB) from the first call on it until the process ends; the first call on
  *    a device takes the array's device address (hipGetSymbolAddress), later
  *    calls reuse it.  No call allocates, frees or synchronises.
@@ -262,7 +265,7 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_rout
  *    live inside the array (device pointers, valid until the next call).
  *  - Unlike the other entry points this one keeps mutable global state: the
  *    per-device addresses of the array (set once, under a lock). */
-#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 moe_status_t moe_forward_noalloc(const moe_shape_t* s, const void* x, const void* w_router, const float* bias,
                                  const int32_t* topk_ids_in, const float* topk_w_in, const void* w_gate,
                                  const void* w_up, const void* w_down, void* out, moe_forward_views_t* views_out,

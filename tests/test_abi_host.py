@@ -184,7 +184,7 @@ def test_noalloc_size_and_argument_checks_return_before_any_hip_call():
     # HIP call (taking the scratch array's device address)
     lib = _lib.lib()
     fake = ctypes.c_void_p(0x1000)
-    big = _shape(T=512, d=4096, E=8, k=2, F=28672)
+    big = _shape(T=512, d=4096, E=8, k=2, F=57344)
     n = ctypes.c_size_t()
     assert lib.moe_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0 and n.value > _lib.NOALLOC_SCRATCH_BYTES
     assert lib.moe_forward_noalloc(ctypes.byref(big), fake, fake, None, None, None, fake, fake, fake, fake,
@@ -226,9 +226,18 @@ def test_carve_and_workspace_checks():
     assert lib.moe_dispatch_carve(ctypes.byref(s), base, q.dispatch_bytes - 1, ctypes.byref(d)) == 3
     assert lib.moe_dispatch_carve(ctypes.byref(s), base + 4, q.dispatch_bytes, ctypes.byref(d)) == 1
     assert lib.moe_dispatch_carve(ctypes.byref(s), base, q.dispatch_bytes, ctypes.byref(d)) == 0
-    ptrs = [getattr(d, n) for n in _lib.DISPATCH_ARRAYS]
+    assert d.kpart is None  # 40 rows per expert: the down GEMM does not split K
+    ptrs = [getattr(d, n) for n in _lib.DISPATCH_ARRAYS if n != "kpart"]
     assert all(p % 256 == 0 and base <= p < base + q.dispatch_bytes for p in ptrs)
     assert len(set(ptrs)) == len(ptrs)
+    # a shape whose down GEMM splits K (bf16, 160-row tiles, 128 rows per expert) carves the two
+    # [R][d] fp32 planes of partial sums
+    s2 = _shape(T=512, d=512, E=8, k=2, F=256, bm=160)
+    st, q2 = _query(s2)
+    d2 = MoeDispatch()
+    assert st == 0 and lib.moe_dispatch_carve(ctypes.byref(s2), base, q2.dispatch_bytes, ctypes.byref(d2)) == 0
+    assert d2.kpart is not None and d2.kpart % 256 == 0
+    assert d2.kpart + 2 * q2.rows * 512 * 4 <= base + q2.dispatch_bytes
     assert d.tile_rows == q.tile_rows and d.max_tiles == q.max_tiles
     fake = ctypes.c_void_p(0x1000)
     # permute workspace too small
@@ -254,7 +263,7 @@ def test_carve_and_workspace_checks():
 
 def test_views_struct_layout():
     # the Python mirror of moe_forward_views_t: a dispatch struct and 5 pointers
-    assert ctypes.sizeof(MoeDispatch) == 10 * 8 + 8
+    assert ctypes.sizeof(MoeDispatch) == 11 * 8 + 8
     assert ctypes.sizeof(MoeShape) == 9 * 4
     assert ctypes.sizeof(MoeForwardViews) == ctypes.sizeof(MoeDispatch) + 5 * 8
     assert ctypes.sizeof(MoeSizes) == 8 + 4 * 4 + 3 * 8

@@ -1,5 +1,5 @@
-"""GPU parity of the two-width gate+up kernel (bf16, 160-row tile map, at
-least 48 rows per expert): tiles of at most 144 rows run 224 columns per
+"""GPU parity of the two-width gate+up kernel (bf16, 160-row tile map, a
+mean of 48 to 136 rows per expert): tiles of at most 144 rows run 224 columns per
 workgroup, longer tiles 112 columns, in one launch.
 
 Routing is set explicitly so that every kind of unit appears: short last
@@ -25,9 +25,9 @@ torch = pytest.importorskip("torch")
 # name: (d, F, rows per expert (k = 1), weight layout blocked16)
 CASES = {
     "ms10_mix": (256, 448, [150, 144, 145, 73], False),
-    "multi_tile": (128, 320, [330, 320, 161, 0, 49, 16], True),
+    "multi_tile": (128, 320, [330, 320, 161, 0, 49, 16, 10, 10], True),
     "tails_blocked": (256, 320, [96, 130, 150, 60], True),
-    "one_expert_long": (128, 192, [700], False),
+    "one_expert_long": (128, 192, [700, 20, 10, 5, 5, 0], False),
     "ragged_f": (192, 256, [50, 159, 144, 1, 100], False),
 }
 
@@ -56,7 +56,8 @@ def test_two_width_gate_up(name):
         pytest.skip("no GPU")
     wl, inp, ids, w, blocked = _inputs(name)
     print(f"\n[gpu wide] {name}: T={wl.T} d={wl.d} F={wl.F} rows per expert {CASES[name][2]}", flush=True)
-    assert wl.T * 1 // wl.E >= 48
+    mean = -(-wl.T // wl.E)
+    assert 48 <= mean <= 136  # the rows per expert for which moe_forward takes the two-width kernel
     x = dev(inp.x)
     wg, wu, wd = dev(inp.wg), dev(inp.wu), dev(inp.wd)
     if blocked:
@@ -98,3 +99,58 @@ def test_two_width_gate_up(name):
     torch.cuda.synchronize()
     live = torch.from_numpy(np.nonzero(ref_disp["token_of"] >= 0)[0]).cuda()
     assert np.array_equal(bits(h2[live]), bits(v.h[live]))
+
+
+# K-split down GEMM (bf16, 160-row tile map, at least 80 mean rows per
+# expert): name -> (d, F, rows per expert (k = 1), capacity)
+SPLIT = {
+    "odd_k_steps": (256, 192, [150, 60, 100, 160], 0),      # 3 K steps: ranges of 2 and 1
+    "multi_tile": (512, 448, [330, 0, 161, 49, 100], 0),
+    "capacity": (256, 320, [200, 40, 120, 80], 100),          # both passes in one launch
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT))
+def test_split_k_down(name):
+    import grouped_gemm_gemv_amd as M
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    d, F, counts, C = SPLIT[name]
+    E, T = len(counts), sum(counts)
+    assert -(-T // E) >= 80 and (not C or min(-(-T // E), C) >= 80)
+    wl = get_workload("mixtral_t512", T=T, d=d, E=E, k=1, F=F)
+    inp = make_inputs(wl, 0)
+    rng = np.random.default_rng(6)
+    ids = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts)).reshape(T, 1)
+    w = np.ones((T, 1), dtype=np.float32)
+    print(f"\n[gpu split-k] {name}: T={T} d={d} F={F} rows per expert {counts} C={C}", flush=True)
+    shape = M.Shape(T, d, E, 1, F, C, torch.bfloat16, 160)
+    q = M.query(shape)
+    x, wg, wu, wd, ids_d, w_d = dev(inp.x), dev(inp.wg), dev(inp.wu), dev(inp.wd), dev(ids), dev(w)
+    ws = M.workspace(q.forward_ws_bytes)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    v = M.moe_forward(shape, x, None, None, ids_d, w_d, wg, wu, wd, out, ws)
+    torch.cuda.synchronize()
+    assert v.disp.c.kpart  # the shape splits the down GEMM's K loop
+    ref_disp = O.dispatch(ids, E, C, 160)
+    check_dispatch(v.disp.arrays(), ref_disp, E)
+    worst = 0.0
+    for e in range(E):
+        rows, _, y_ref = O.expert_rows(inp.x, inp.wg, inp.wu, inp.wd, "bf16", ref_disp, e)
+        if rows.size:
+            worst = max(worst, rel_err(host64(v.y_perm[torch.from_numpy(rows).cuda()]), y_ref))
+    ref = O.forward(inp.x, inp.wr, inp.wg, inp.wu, inp.wd, 1, "bf16", topk_ids=ids, topk_w=w, capacity=C)["out"]
+    err = rel_err(host64(out), ref)
+    print(f"[gpu split-k] {name}: y_perm rel err (worst expert) {worst:.3e}, layer rel err {err:.3e}", flush=True)
+    assert worst <= TOL["bf16"] and err <= TOL["bf16"]
+    # repeated down launches and whole layers give the same bits
+    y0 = v.y_perm.clone()
+    ps = M.PASS_BOTH if C else 0
+    for _ in range(3):
+        M.moe_ffn_down(shape, v.h, wd, v.disp, ps, v.y_perm)
+    out2 = torch.empty_like(out)
+    M.moe_forward(shape, x, None, None, ids_d, w_d, wg, wu, wd, out2, ws)
+    torch.cuda.synchronize()
+    live = torch.from_numpy(np.nonzero(ref_disp["token_of"] >= 0)[0]).cuda()
+    assert np.array_equal(bits(v.y_perm[live]), bits(y0[live]))
+    assert np.array_equal(bits(out2), bits(out))

@@ -69,7 +69,7 @@ def test_noalloc_rejects_shapes_past_the_scratch_size():
     from grouped_gemm_gemv_amd._lib import NOALLOC_SCRATCH_BYTES, MoeError
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    shape = M.Shape(512, 4096, 8, 2, 14336 * 2, 0, torch.bfloat16)
+    shape = M.Shape(512, 4096, 8, 2, 14336 * 4, 0, torch.bfloat16)
     assert M.workspace_size(shape) > NOALLOC_SCRATCH_BYTES
     x = torch.zeros((512, 4096), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((1, 64), dtype=torch.bfloat16, device="cuda")  # never read: rejected before any launch
