@@ -373,7 +373,7 @@ moe_status_t enqueue_down(const moe_shape_t& s, const void* h, const void* wd, c
                           void* y, hipStream_t st, const float* sd = nullptr) {
   moe::GemmArgs a = gemm_args(s, d, pass, false);
   a.s0 = sd;
-  const bool split = sd == nullptr && split_down(s, d.tile_rows);
+  const bool split = split_down(s, d.tile_rows);
   if (split) {
     a.kpart = d.kpart;
     a.kplane = (size_t)row_space(s) * s.d;

@@ -96,7 +96,7 @@ template <> struct TileCfg<192, false> { using type = TileShape<192, 32, 8, 1, 2
 // 128 columns per workgroup, half the LDS reads per MFMA (T = 512: 154 vs
 // 159 us; decode T = 256: 93 vs 102 us).
 template <> struct TileCfg<160, false, true> { using type = TileShape<160, 32, 4, 1, 4, 10>; };
-// bf16 down on the 160-row tile map with many rows per expert: 256 output
+// bf16 down (bf16 or E4M3 weights) on the 160-row tile map with many rows per expert: 256 output
 // columns per workgroup (32 per wavefront) with the K loop split in two
 // ranges worked by two workgroups (KS = 2 in grouped_gemm_kernel), so the
 // workgroup count stays that of 128-column tiles while each activation byte

@@ -746,8 +746,8 @@ hipError_t dispatch_bm(int BM, const GemmArgs& a, hipStream_t stream) {
   if constexpr (GATED && !WQ && std::is_same<Tr, TBF16>::value) {
     if (BM == 160 && a.wide && a.tile_off2 == nullptr) return launch_wide<Tr, Wide160>(a, stream);
   }
-  if constexpr (!GATED && !WQ && std::is_same<Tr, TBF16>::value) {
-    if (BM == 160 && a.kpart != nullptr) return launch_cfg<Tr, Split160, false, false, 2>(a, stream);
+  if constexpr (!GATED && std::is_same<Tr, TBF16>::value) {
+    if (BM == 160 && a.kpart != nullptr) return launch_cfg<Tr, Split160, false, WQ, 2>(a, stream);
   }
   switch (BM) {
 #define MOE_BM_CASE(bm) \
