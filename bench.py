@@ -68,6 +68,11 @@ def parse():
                          "for n from 1 to 1024, fit t = max(a, c + b*n) and exit")
     ap.add_argument("--cost-experts", type=int, default=8, help="experts per launch for --cost-curve")
     ap.add_argument("--cost-tile-rows", type=int, default=0, help="tile height for --cost-curve (0: automatic)")
+    ap.add_argument("--stall-summary", nargs="+", metavar="DB",
+                    help="per grouped-GEMM kernel: TA/TD busy and stall cycles and matrix-core busy cycles as a "
+                         "fraction of the kernel's cycles, from PMC runs that together hold GRBM_GUI_ACTIVE, "
+                         "TA_TA_BUSY_sum, TD_TD_BUSY_sum, TD_TC_STALL_sum, TCP_PENDING_STALL_CYCLES_sum, "
+                         "TA_ADDR_STALLED_BY_TC_CYCLES_sum and SQ_VALU_MFMA_BUSY_CYCLES; then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print the grouped-GEMM HBM traffic from a FETCH_SIZE and a WRITE_SIZE run "
                          "(both with --pmc-calibration) and exit")
@@ -191,6 +196,42 @@ def pmc_summary(fetch_db: str, write_db: str, workload: str):
         f, _ = out[(key, "FETCH_SIZE")]
         w, _ = out[(key, "WRITE_SIZE")]
         print(f"{key}_hbm_bytes_per_launch: {round((f * sf + w * sw) * 1024)}")
+
+
+def stall_summary(dbs):
+    """Busy and stall fractions of the grouped-GEMM kernels from PMC runs.
+
+    Counter values are summed over the instances the profiler reports and
+    averaged over dispatches: GRBM_GUI_ACTIVE counts cycles of each of the 8
+    XCDs, the TA/TD/TCP counters cycles of each of the 256 compute units, and
+    SQ_VALU_MFMA_BUSY_CYCLES cycles of each of the 1024 SIMDs, so each ratio
+    below is a per-unit fraction of the kernel's cycles."""
+    import collections
+    import sqlite3
+    vals = collections.defaultdict(list)
+    for db_path in dbs:
+        db = sqlite3.connect(db_path)
+        per = collections.defaultdict(float)
+        for name, did, cn, cv in db.execute("select name, dispatch_id, counter_name, counter_value from pmc_events"):
+            role = gemm_role(name)
+            if role is not None:
+                per[(role, cn, did)] += cv
+        for (role, cn, _), v in per.items():
+            vals[(role, cn)].append(v)
+    mean = {k: sum(v) / len(v) for k, v in vals.items()}
+    print("# kernel | cycles per XCD | TA busy | TD busy | TD stalled on L1 | L1 stalled on L2 | TA address "
+          "stalled on L1 | matrix cores busy (per SIMD) | dispatches")
+    for role in ("gateup", "down"):
+        if (role, "GRBM_GUI_ACTIVE") not in mean:
+            continue
+        cyc = mean[(role, "GRBM_GUI_ACTIVE")] / 8
+
+        def f(counter, units=256):
+            v = mean.get((role, counter))
+            return "n/a" if v is None else f"{v / units / cyc * 100:.0f} %"
+        print(f"{role} | {cyc:,.0f} | {f('TA_TA_BUSY_sum')} | {f('TD_TD_BUSY_sum')} | {f('TD_TC_STALL_sum')} | "
+              f"{f('TCP_PENDING_STALL_CYCLES_sum')} | {f('TA_ADDR_STALLED_BY_TC_CYCLES_sum')} | "
+              f"{f('SQ_VALU_MFMA_BUSY_CYCLES', 1024)} | {len(vals[(role, 'GRBM_GUI_ACTIVE')])}")
 
 
 def kernel_table(fetch_db: str, write_db: str, trace_db: str):
@@ -486,6 +527,9 @@ def main():
         return
     if args.kernel_table:
         kernel_table(*args.kernel_table)
+        return
+    if args.stall_summary:
+        stall_summary(args.stall_summary)
         return
     if args.cost_curve:
         if args.gpus != 1:
