@@ -95,21 +95,9 @@ def dispatch(ids, E: int, capacity: int, tile_rows: int) -> Dict[str, list]:
                 left -= n
                 i += 1
             tile_off[p].append(len(tile_map[p]))
-    # largest-expert-first: repeatedly take the expert with the most tiles
-    # (both passes) not taken yet, the lowest index among equals
-    tiles = [sum(1 for p in range(2) for tm in tile_map[p] if tm[0] == e) for e in range(E)]
-    order, left = [], list(range(E))
-    while left:
-        best = left[0]
-        for e in left:
-            if tiles[e] > tiles[best]:
-                best = e
-        order.append(best)
-        left.remove(best)
     return {"counts": counts, "offsets": offsets, "spill_counts": spill,
             "spill_offsets": spill_off, "rank": rank, "row_of": row_of,
-            "token_of": token_of, "R": R, "tile_off": tile_off, "tile_map": tile_map,
-            "expert_order": order}
+            "token_of": token_of, "R": R, "tile_off": tile_off, "tile_map": tile_map}
 
 
 def hidden(xrow, wg, wu):

@@ -303,24 +303,7 @@ def dispatch(ids: np.ndarray, E: int, capacity: int = 0, tile_rows: int = 16) ->
         "pass_base": np.stack(base), "pass_rows": np.stack(rows),
         "tile_off": tile_off, "tile_map": tile_map,
         "n_tiles": np.array([len(tile_map[0]), len(tile_map[1])]),
-        "expert_order": expert_order(tile_off),
     }
-
-
-def expert_order(tile_off: np.ndarray) -> np.ndarray:
-    """Largest-expert-first order of the block schedule.
-
-    Reading of the TritonMoE review's skeptic critique (section 4.7: a fixed
-    block schedule loses under skewed expert loads) and of the test its
-    desk-editor letter asks for (blocks recomputed after sorting the experts
-    by load): the experts listed from the most row tiles to the fewest,
-    counting the tiles of both passes together, equal counts in ascending
-    expert index.  Only the order in which the grouped GEMMs take up the
-    experts' tiles changes; the tile map and every row stay where they are.
-    """
-    t = np.asarray(tile_off, dtype=np.int64)
-    tiles = (t[0, 1:] - t[0, :-1]) + (t[1, 1:] - t[1, :-1])
-    return np.array(sorted(range(len(tiles)), key=lambda e: (-int(tiles[e]), e)), dtype=np.int64)
 
 
 def gather(x: np.ndarray, disp: Dict[str, np.ndarray]) -> np.ndarray:
