@@ -49,6 +49,9 @@ CASES = {
     "bf16_cap_no_spill": ("capacity_gini0.30", dict(T=64, d=128, E=8, k=2, F=128, capacity=128)),
     "bf16_cap_c1": ("capacity_gini0.30", dict(T=100, d=64, E=8, k=2, F=64, capacity=1)),
     "bf16_one_expert": ("e64_zipf_a2.0", dict(T=300, d=128, E=16, k=1, F=128, zipf_alpha=60.0)),
+    # a few dominant experts among 64 (the top Zipf ranks take nearly every
+    # token), each with several row tiles, beside many one-tile experts
+    "bf16_dominant_e64": ("e64_zipf_a2.0", dict(T=600, d=128, F=192, zipf_alpha=4.0)),
     "bf16_e256_k64": ("mixtral_t512", dict(T=33, d=64, E=256, k=64, F=64)),
     # decode batches: one router workgroup and the one-block dispatch, at the
     # sizes of each router tile (E <= 16, 32, 64), and the first T past 16
