@@ -250,6 +250,30 @@ moe_status_t check_dispatch(const moe_shape_t& s, const Plan& p, const moe_dispa
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+moe::SmallDispatchArgs small_dispatch_args(const moe_shape_t& s, const Plan& p, const int32_t* ids,
+                                           const moe_dispatch_t& d) {
+  moe::SmallDispatchArgs a;
+  a.ids = ids;
+  a.Tk = (int)p.Tk;
+  a.k = s.k;
+  a.E = s.E;
+  a.C = s.capacity;
+  a.BM = d.tile_rows;
+  a.max_tiles = d.max_tiles;
+  a.rows = p.R;
+  a.counts = d.counts;
+  a.offsets = d.offsets;
+  a.spill_counts = d.spill_counts;
+  a.spill_offsets = d.spill_offsets;
+  a.row_of = d.row_of;
+  a.token_of = d.token_of;
+  a.tile_off = d.tile_off;
+  a.tile_map = d.tile_map;
+  a.n_tiles = d.n_tiles;
+  a.err_flags = d.err_flags;
+  return a;
+}
+
 // Dispatch (count, scan, ranks, tile map) and, if x_perm is not null, the gather.
 moe_status_t enqueue_permute(const moe_shape_t& s, const Plan& p, const void* x, const int32_t* ids,
                              const moe_dispatch_t& d, void* x_perm, void* ws, hipStream_t st) {
@@ -258,26 +282,7 @@ moe_status_t enqueue_permute(const moe_shape_t& s, const Plan& p, const void* x,
   uint32_t* block_err = reinterpret_cast<uint32_t*>(w + align_up(4 * (size_t)p.nblk * s.E));
   const int Tk = (int)p.Tk;
   if (Tk <= moe::kSmallDispatch) {
-    moe::SmallDispatchArgs a;
-    a.ids = ids;
-    a.Tk = Tk;
-    a.k = s.k;
-    a.E = s.E;
-    a.C = s.capacity;
-    a.BM = d.tile_rows;
-    a.max_tiles = d.max_tiles;
-    a.rows = p.R;
-    a.counts = d.counts;
-    a.offsets = d.offsets;
-    a.spill_counts = d.spill_counts;
-    a.spill_offsets = d.spill_offsets;
-    a.row_of = d.row_of;
-    a.token_of = d.token_of;
-    a.tile_off = d.tile_off;
-    a.tile_map = d.tile_map;
-    a.n_tiles = d.n_tiles;
-    a.err_flags = d.err_flags;
-    if (moe::launch_dispatch_small(a, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_dispatch_small(small_dispatch_args(s, p, ids, d), st) != hipSuccess) return MOE_ERR_HIP;
     if (x_perm == nullptr) return MOE_OK;
     return hip_status(moe::launch_gather(x, d.row_of, Tk, s.k, (int64_t)s.d * elt_bytes(s), x_perm, st));
   }
@@ -421,12 +426,18 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_rou
     v.topk_w = reinterpret_cast<float*>(ws + p.ws_w);
   }
   if (views_out != nullptr) *views_out = v;
-  if (topk_ids_in == nullptr) {
-    if (moe::launch_route(s->dtype, x, w_router, bias, s->T, s->d, s->E, s->k, v.topk_ids, v.topk_w, stream) !=
-        hipSuccess)
+  if (topk_ids_in == nullptr && s->T <= moe::kRouteDispatchTokens && s->E <= 64) {
+    // a decode batch: routing and dispatch in one workgroup
+    if (moe::launch_route_dispatch(s->dtype, x, w_router, bias, s->T, s->d, s->E, s->k, v.topk_ids, v.topk_w,
+                                   small_dispatch_args(*s, p, v.topk_ids, v.disp), stream) != hipSuccess)
       return MOE_ERR_HIP;
+  } else {
+    if (topk_ids_in == nullptr &&
+        moe::launch_route(s->dtype, x, w_router, bias, s->T, s->d, s->E, s->k, v.topk_ids, v.topk_w, stream) !=
+            hipSuccess)
+      return MOE_ERR_HIP;
+    if ((st = enqueue_permute(*s, p, x, v.topk_ids, v.disp, nullptr, ws + p.ws_perm, stream)) != MOE_OK) return st;
   }
-  if ((st = enqueue_permute(*s, p, x, v.topk_ids, v.disp, nullptr, ws + p.ws_perm, stream)) != MOE_OK) return st;
   // capacity mode: both passes in each launch (the overflow tiles of an expert
   // run next to its first-pass tiles and find its weights in L2)
   const int ps = s->capacity > 0 ? kBothPasses : 0;

@@ -21,9 +21,12 @@
 //             expert id) plus an LDS prefix across wavefronts and rounds.
 //   dispatch_small : all of the above in one 1024-thread block when T*k is
 //             at most kSmallDispatch (one launch instead of three).
+//   dispatch_tiny : the same by one wavefront with no barrier, for at most
+//             64 entries over at most 64 experts (a decode step).
 //   gather  : one wavefront per entry, 16-byte vector row copy.
 //   combine : one workgroup per token, fp32 weighted sum in slot order.
 #include "device_common.hpp"
+#include "dispatch_small.hpp"
 #include "launch.hpp"
 
 namespace moe {
@@ -54,31 +57,6 @@ __global__ __launch_bounds__(kThreads) void count_kernel(const int32_t* __restri
   // capacity mode: mark every row unused before the scatter fills live rows
   for (int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x; r < fill_rows; r += (int64_t)gridDim.x * kThreads)
     token_of[r] = -1;
-}
-
-// Exclusive scan of one int per thread over a block of NW wavefronts; every
-// thread of the block must call it.  `tmp` holds NW ints of LDS.
-template <int NW>
-__device__ int block_exclusive_scan(int v, int* tmp, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(inc, o);
-    if (lane >= o) inc += n;
-  }
-  if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int t = tmp[w];
-    before += (w < wave) ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return before + inc - v;
 }
 
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
@@ -291,124 +269,9 @@ __global__ __launch_bounds__(kThreads) void k_split_finish_kernel(const float* _
   }
 }
 
-// Whole dispatch (count, scans, capacity split, tile map, stable ranks) in
-// one workgroup of 1024 threads, for T*k up to kSmallDispatch: one launch
-// instead of three.  Same results as count + scan + scatter.
-__global__ __launch_bounds__(1024) void dispatch_small_kernel(SmallDispatchArgs a) {
-  constexpr int NW = 16;
-  __shared__ int hist[256];
-  __shared__ int run[256];
-  __shared__ int wcnt[NW][256];
-  __shared__ int tmp[NW];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int E = a.E, C = a.C, BM = a.BM;
-  for (int i = tid; i < 256; i += 1024) {
-    hist[i] = 0;
-    run[i] = 0;
-  }
-  for (int i = tid; i < NW * 256; i += 1024) (&wcnt[0][0])[i] = 0;
-  for (int64_t r = tid; r < a.rows; r += 1024) a.token_of[r] = -1;
-  __syncthreads();
-  int bad = 0;
-  for (int f = tid; f < a.Tk; f += 1024) {
-    const int e = a.ids[f];
-    if ((unsigned)e < (unsigned)E)
-      atomicAdd(&hist[e], 1);
-    else
-      bad = 1;
-  }
-  bad = __syncthreads_or(bad);
-  const bool ok = tid < E;
-  const int n = ok ? hist[tid] : 0;
-  int total;
-  const int off = block_exclusive_scan<NW>(n, tmp, total);
-  const int kept = ok ? (C > 0 ? min(n, C) : n) : 0;
-  const int spill = ok ? (C > 0 ? max(n - C, 0) : 0) : 0;
-  int spill_total;
-  const int spill_off = block_exclusive_scan<NW>(spill, tmp, spill_total);
-  if (ok) {
-    a.counts[tid] = n;
-    a.offsets[tid] = off;
-    a.spill_counts[tid] = spill;
-    a.spill_offsets[tid] = spill_off;
-    hist[tid] = off;          // now: first row of expert tid (uncapped)
-    run[tid] = spill_off;     // now: first overflow row of expert tid, relative to E*C
-  }
-  if (tid == 0) {
-    a.offsets[E] = total;
-    a.spill_offsets[E] = spill_total;
-    a.err_flags[0] = bad ? 1u : 0u;
-  }
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int rows = (p == 0) ? kept : spill;
-    const int base = (p == 0) ? (C > 0 ? tid * C : off) : E * C + spill_off;
-    const int tiles = (rows + BM - 1) / BM;
-    int ntiles;
-    const int toff = block_exclusive_scan<NW>(tiles, tmp, ntiles);
-    int32_t* tile_off = a.tile_off + p * (E + 1);
-    int32_t* tile_map = a.tile_map + (size_t)p * a.max_tiles * 4;
-    if (ok) tile_off[tid] = toff;
-    if (tid == 0) {
-      tile_off[E] = ntiles;
-      a.n_tiles[p] = ntiles;
-    }
-    for (int i = 0; i < tiles; ++i) {
-      int4 ent;
-      ent.x = tid;
-      ent.y = base + i * BM;
-      ent.z = min(BM, rows - i * BM);
-      ent.w = i;
-      reinterpret_cast<int4*>(tile_map)[toff + i] = ent;
-    }
-  }
-  // stable ranks: rounds of 1024 entries in ascending f
-  __shared__ int rank_base[256];
-  for (int i = tid; i < 256; i += 1024) rank_base[i] = 0;
-  __syncthreads();
-  const int nbits = (E <= 1) ? 0 : 32 - __clz(E - 1);
-  const uint64_t lt = lanemask_lt(lane);
-  for (int f0 = 0; f0 < a.Tk; f0 += 1024) {
-    const int f = f0 + tid;
-    const bool valid = f < a.Tk;
-    const int e = valid ? a.ids[f] : -1;
-    const bool eok = valid && (unsigned)e < (unsigned)E;
-    uint64_t m = __ballot(eok);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = eok && ((e >> b) & 1);
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
-    }
-    const int lrank = __popcll(m & lt);
-    if (eok && lrank == 0) wcnt[wave][e] = __popcll(m);
-    __syncthreads();
-    if (eok) {
-      int g = rank_base[e] + lrank;
-      for (int w = 0; w < wave; ++w) g += wcnt[w][e];
-      int row;
-      if (C > 0)
-        row = (g < C) ? e * C + g : E * C + run[e] + (g - C);
-      else
-        row = hist[e] + g;
-      a.row_of[f] = row;
-      a.token_of[row] = f / a.k;
-    } else if (valid) {
-      a.row_of[f] = -1;
-    }
-    __syncthreads();
-    for (int i = tid; i < E; i += 1024) {
-      int sum = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        sum += wcnt[w][i];
-        wcnt[w][i] = 0;
-      }
-      rank_base[i] += sum;
-    }
-    __syncthreads();
-  }
-}
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(SmallDispatchArgs a) { dispatch_block(a, a.ids); }
+
+__global__ __launch_bounds__(64) void dispatch_tiny_kernel(SmallDispatchArgs a) { dispatch_wave(a, a.ids); }
 
 }  // namespace
 
@@ -440,7 +303,10 @@ hipError_t launch_gather(const void* x, const int32_t* row_of, int Tk, int k, in
 }
 
 hipError_t launch_dispatch_small(const SmallDispatchArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, stream, a);
+  if (tiny_dispatch(a.Tk, a.E, a.rows))
+    hipLaunchKernelGGL(dispatch_tiny_kernel, dim3(1), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

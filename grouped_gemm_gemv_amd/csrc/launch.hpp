@@ -34,6 +34,13 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 
 // Entries up to which one 1024-thread block does the whole dispatch.
 constexpr int kSmallDispatch = 16384;
+// Limits of the one-wavefront dispatch (a decode step): entries, experts, rows.
+constexpr int kTinyDispatchEntries = 64;
+constexpr int kTinyDispatchExperts = 64;
+constexpr int kTinyDispatchRows = 4096;
+__host__ __device__ inline bool tiny_dispatch(int Tk, int E, int64_t rows) {
+  return Tk <= kTinyDispatchEntries && E <= kTinyDispatchExperts && rows <= kTinyDispatchRows;
+}
 
 struct SmallDispatchArgs {
   const int32_t* ids;
@@ -51,6 +58,13 @@ struct SmallDispatchArgs {
   uint32_t* err_flags;
 };
 hipError_t launch_dispatch_small(const SmallDispatchArgs& a, hipStream_t stream);
+
+// Tokens up to which a batch with router weights (E <= 64) is routed and
+// dispatched by one workgroup in one launch (a.ids must be topk_ids).
+constexpr int kRouteDispatchTokens = 16;
+hipError_t launch_route_dispatch(int dtype, const void* x, const void* w_router, const float* bias, int T, int d,
+                                 int E, int k, int32_t* topk_ids, float* topk_w, const SmallDispatchArgs& a,
+                                 hipStream_t stream);
 
 hipError_t launch_scatter(const int32_t* ids, int Tk, int k, int E, int C, int nblk,
                           const int32_t* block_base, const int32_t* offsets, const int32_t* spill_offsets,

@@ -19,6 +19,7 @@
 #include <float.h>
 
 #include "device_common.hpp"
+#include "dispatch_small.hpp"
 #include "launch.hpp"
 
 namespace moe {
@@ -29,12 +30,13 @@ namespace {
 // columns; fewer tokens spread a small batch over more compute units, while
 // a large batch is better served by 16, since every workgroup reads all of
 // the router weights).
+// Routing of tokens t0 .. t0 + kTok - 1 by one workgroup of 64 * KW threads
+// (every thread calls it).  ids_lds, if not null, also receives the chosen
+// experts, in LDS at [t - t0][j], for a kernel that dispatches next.
 template <class Tr, int NS, int KW, int U, int kTok>
-__global__ __launch_bounds__(64 * KW) void route_kernel(const typename Tr::T* __restrict__ x,
-                                                        const typename Tr::T* __restrict__ wr,
-                                                        const float* __restrict__ bias, int T, int d, int E,
-                                                        int k, int32_t* __restrict__ topk_ids,
-                                                        float* __restrict__ topk_w) {
+__device__ void route_block(const typename Tr::T* __restrict__ x, const typename Tr::T* __restrict__ wr,
+                            const float* __restrict__ bias, int T, int d, int E, int k, int t0,
+                            int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* ids_lds) {
   using Elt = typename Tr::T;
   constexpr int E16 = NS * 16;
   __shared__ float part[KW][E16][kTok];  // per-wavefront partial logits
@@ -44,7 +46,6 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(const typename Tr::T* __
   // uniform in the wavefront; saying so keeps the slab index, and with it the
   // loads' K offset, in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t0 = blockIdx.x * kTok;
   const int ntok = min(kTok, T - t0);
   const int row_bytes = d * (int)sizeof(Elt);
   const int nslab = row_bytes / 64;
@@ -144,7 +145,36 @@ __global__ __launch_bounds__(64 * KW) void route_kernel(const typename Tr::T* __
     if (lane < k) {
       topk_ids[(size_t)t * k + lane] = my_id;
       topk_w[(size_t)t * k + lane] = ex / sum;
+      if (ids_lds != nullptr) ids_lds[tt * k + lane] = my_id;
     }
+  }
+}
+
+template <class Tr, int NS, int KW, int U, int kTok>
+__global__ __launch_bounds__(64 * KW) void route_kernel(const typename Tr::T* __restrict__ x,
+                                                        const typename Tr::T* __restrict__ wr,
+                                                        const float* __restrict__ bias, int T, int d, int E,
+                                                        int k, int32_t* __restrict__ topk_ids,
+                                                        float* __restrict__ topk_w) {
+  route_block<Tr, NS, KW, U, kTok>(x, wr, bias, T, d, E, k, (int)blockIdx.x * kTok, topk_ids, topk_w, nullptr);
+}
+
+// A decode batch (T <= kRouteDispatchTokens, E <= 64) routed and dispatched
+// by one workgroup: the chosen experts pass to the dispatch in LDS, with no
+// second launch and no round trip through global memory.
+template <class Tr, int NS, int U>
+__global__ __launch_bounds__(1024) void route_dispatch_kernel(const typename Tr::T* __restrict__ x,
+                                                              const typename Tr::T* __restrict__ wr,
+                                                              const float* __restrict__ bias, int T, int d,
+                                                              int E, int k, int32_t* __restrict__ topk_ids,
+                                                              float* __restrict__ topk_w, SmallDispatchArgs a) {
+  __shared__ int32_t ids[kRouteDispatchTokens * 64];
+  route_block<Tr, NS, 16, U, kRouteDispatchTokens>(x, wr, bias, T, d, E, k, 0, topk_ids, topk_w, ids);
+  __syncthreads();
+  if (tiny_dispatch(a.Tk, a.E, a.rows)) {
+    if (threadIdx.x < 64) dispatch_wave(a, ids);
+  } else {
+    dispatch_block(a, ids);
   }
 }
 
@@ -168,7 +198,34 @@ hipError_t launch_t(const void* x, const void* w_router, const float* bias, int 
   return hipGetLastError();
 }
 
+template <class Tr>
+hipError_t launch_rd(const void* x, const void* w_router, const float* bias, int T, int d, int E, int k,
+                     int32_t* topk_ids, float* topk_w, const SmallDispatchArgs& a, hipStream_t stream) {
+  using Elt = typename Tr::T;
+  const Elt* xp = static_cast<const Elt*>(x);
+  const Elt* wp = static_cast<const Elt*>(w_router);
+  if (E <= 16)
+    hipLaunchKernelGGL((route_dispatch_kernel<Tr, 1, 8>), dim3(1), dim3(1024), 0, stream, xp, wp, bias, T, d, E, k,
+                       topk_ids, topk_w, a);
+  else if (E <= 32)
+    hipLaunchKernelGGL((route_dispatch_kernel<Tr, 2, 8>), dim3(1), dim3(1024), 0, stream, xp, wp, bias, T, d, E, k,
+                       topk_ids, topk_w, a);
+  else
+    hipLaunchKernelGGL((route_dispatch_kernel<Tr, 4, 4>), dim3(1), dim3(1024), 0, stream, xp, wp, bias, T, d, E, k,
+                       topk_ids, topk_w, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_route_dispatch(int dtype, const void* x, const void* w_router, const float* bias, int T, int d,
+                                 int E, int k, int32_t* topk_ids, float* topk_w, const SmallDispatchArgs& a,
+                                 hipStream_t stream) {
+  if (T < 1 || T > kRouteDispatchTokens || E > 64 || a.ids != topk_ids || a.Tk != T * k)
+    return hipErrorInvalidValue;
+  if (dtype == 1) return launch_rd<TBF16>(x, w_router, bias, T, d, E, k, topk_ids, topk_w, a, stream);
+  return launch_rd<TF32>(x, w_router, bias, T, d, E, k, topk_ids, topk_w, a, stream);
+}
 
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* bias, int T, int d,
                         int E, int k, int32_t* topk_ids, float* topk_w, hipStream_t stream) {

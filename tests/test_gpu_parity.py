@@ -53,11 +53,16 @@ CASES = {
     # token), each with several row tiles, beside many one-tile experts
     "bf16_dominant_e64": ("e64_zipf_a2.0", dict(T=600, d=128, F=192, zipf_alpha=4.0)),
     "bf16_e256_k64": ("mixtral_t512", dict(T=33, d=64, E=256, k=64, F=64)),
-    # decode batches: one router workgroup and the one-block dispatch, at the
-    # sizes of each router tile (E <= 16, 32, 64), and the first T past 16
+    # decode batches (T <= 16, E <= 64): moe_forward routes and dispatches
+    # them in one workgroup (route_dispatch_kernel), which the step-by-step
+    # path (moe_route, then moe_permute) checks bitwise, at each router tile
+    # (E <= 16, 32, 64), with a router bias and the capacity split; T = 17
+    # takes the separate router and dispatch launches in moe_forward too
     "bf16_t8": ("mixtral_t512", dict(T=8, d=256, F=128)),
     "bf16_t16_e64": ("mixtral_t512", dict(T=16, d=256, E=64, k=6, F=128)),
+    "bf16_t1_e64": ("mixtral_t512", dict(T=1, d=128, E=64, k=8, F=64)),
     "f32_t16_e32": ("tiny_f32", dict(T=16, E=32, k=4)),
+    "bf16_t12_cap_bias": ("capacity_gini0.30", dict(T=12, d=128, E=16, k=4, F=128, capacity=2)),
     "bf16_t17": ("mixtral_t512", dict(T=17, d=128, F=64)),
     # 384-row tiles, worked in pieces (three of 128 rows by gate+up, two of
     # 192 by down): experts of two and three map tiles with ragged and empty
@@ -322,6 +327,67 @@ def test_dispatch_multiblock_path(C):
     xb = bits(x)
     live = ref["token_of"] >= 0
     assert np.array_equal(bits(xp)[live], xb[ref["token_of"][live]])
+
+
+# (T, k, E, C, invalid ids): one-wavefront dispatch (T*k <= 64, E <= 64,
+# rows <= 4096) at its limits, with the capacity split, dead rows and
+# invalid ids; and the same kinds of input just past each limit (1024-thread
+# block)
+TINY = {
+    "t1_k2": (1, 2, 8, 0, False),
+    "tk64_e8": (32, 2, 8, 0, False),
+    "tk64_e64": (64, 1, 64, 0, False),
+    "cap_overflow": (16, 4, 16, 3, False),
+    "cap_rows_4032": (1, 1, 64, 63, False),
+    "bad_ids": (20, 3, 10, 0, True),
+    "cap_bad_ids": (20, 2, 8, 2, True),
+    "tk65_block": (65, 1, 8, 0, False),
+    "e65_block": (8, 2, 65, 0, True),
+    "rows_4160_block": (1, 1, 64, 65, False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TINY))
+def test_small_dispatch_paths(name):
+    """Dispatch of small batches against the oracle, array by array.  Invalid
+    ids (outside [0, E)) are skipped: every other entry gets the row and rank
+    the oracle gives the batch without them, so the expected arrays are the
+    oracle's dispatch of the valid entries (one per row, k = 1), mapped back
+    to their flat index f and token f // k."""
+    _need_gpu()
+    import grouped_gemm_gemv_amd as M
+    T, k, E, C, bad = TINY[name]
+    rng = np.random.default_rng(11)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if bad:
+        ids[1, 0] = E
+        ids[T - 2, k - 1] = -1
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    fv = np.nonzero(valid)[0]
+    shape = M.Shape(T=T, d=64, E=E, k=k, F=64, capacity=C, dtype=torch.bfloat16)
+    q = M.query(shape)
+    print(f"\n[gpu parity] small dispatch {name}: T={T} k={k} E={E} C={C} rows={q.rows}", flush=True)
+    x = torch.randn((T, 64), device="cuda").to(torch.bfloat16)
+    disp = M.Dispatch(shape)
+    xp = torch.zeros((q.rows, 64), dtype=torch.bfloat16, device="cuda")
+    M.moe_permute(shape, x, dev(ids), disp, xp, M.workspace(q.permute_ws_bytes))
+    torch.cuda.synchronize()
+    sub = O.dispatch(flat[fv].reshape(-1, 1), E, C, q.tile_rows)
+    ref = dict(sub)
+    ref["row_of"] = np.full(T * k, -1, dtype=np.int64)
+    ref["row_of"][fv] = sub["row_of"]
+    ref["token_of"] = np.full(q.rows, -1, dtype=np.int64)
+    live = sub["token_of"] >= 0
+    ref["token_of"][np.nonzero(live)[0]] = fv[sub["token_of"][live]] // k
+    a = disp.arrays()
+    assert int(a["err_flags"].cpu().numpy()[0]) == (1 if bad else 0)
+    a = dict(a)
+    a["err_flags"] = torch.zeros_like(a["err_flags"])
+    check_dispatch(a, ref, E)
+    xb = bits(x)
+    rows = ref["token_of"] >= 0
+    assert np.array_equal(bits(xp)[rows], xb[ref["token_of"][rows]])
 
 
 def test_invalid_ids_flagged_and_skipped():
