@@ -374,8 +374,11 @@ moe_status_t enqueue_gate_up(const moe_shape_t& s, const void* x_perm, const voi
   return hip_status(moe::launch_grouped_gemm(s.dtype, true, d.tile_rows, a, st));
 }
 
+// Down GEMM over one pass.  With the K loop split (split_down), the two fp32
+// partial planes are added into y by k_split_finish unless `finish` is false
+// (moe_forward then forms y inside its combine).
 moe_status_t enqueue_down(const moe_shape_t& s, const void* h, const void* wd, const moe_dispatch_t& d, int pass,
-                          void* y, hipStream_t st, const float* sd = nullptr) {
+                          void* y, hipStream_t st, const float* sd = nullptr, bool finish = true) {
   moe::GemmArgs a = gemm_args(s, d, pass, false);
   a.s0 = sd;
   const bool split = split_down(s, d.tile_rows);
@@ -388,7 +391,7 @@ moe_status_t enqueue_down(const moe_shape_t& s, const void* h, const void* wd, c
   a.w1 = nullptr;
   a.out = y;
   moe_status_t st_ = hip_status(moe::launch_grouped_gemm(s.dtype, false, d.tile_rows, a, st));
-  if (st_ != MOE_OK || !split) return st_;
+  if (st_ != MOE_OK || !split || !finish) return st_;
   // y rows of the pass(es) just computed: the uncapped rows or the fixed
   // region (pass 0), the overflow region (pass 1)
   const int64_t fixed = s.capacity > 0 ? (int64_t)s.E * s.capacity : row_space(s);
@@ -443,7 +446,11 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_rou
   const int ps = s->capacity > 0 ? kBothPasses : 0;
   if ((st = enqueue_gate_up(*s, nullptr, w_gate, w_up, v.disp, ps, v.h, stream, x, s_gate, s_up)) != MOE_OK)
     return st;
-  if ((st = enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream, s_down)) != MOE_OK) return st;
+  const bool split = split_down(*s, v.disp.tile_rows);
+  if ((st = enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream, s_down, !split)) != MOE_OK) return st;
+  if (split)  // y formed from the two K ranges inside the combine
+    return hip_status(moe::launch_combine_split(s->dtype, v.disp.kpart, (size_t)p.R * s->d, v.topk_w,
+                                                v.disp.row_of, s->T, s->k, s->d, v.y_perm, out, stream));
   return hip_status(
       moe::launch_combine(s->dtype, v.y_perm, v.topk_w, v.disp.row_of, s->T, s->k, s->d, out, stream));
 }

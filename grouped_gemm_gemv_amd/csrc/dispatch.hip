@@ -25,6 +25,8 @@
 //             64 entries over at most 64 experts (a decode step).
 //   gather  : one wavefront per entry, 16-byte vector row copy.
 //   combine : one workgroup per token, fp32 weighted sum in slot order.
+//   combine_split : the same from the split down GEMM's two fp32 partial
+//             planes, storing each live y row on the way.
 #include "device_common.hpp"
 #include "dispatch_small.hpp"
 #include "launch.hpp"
@@ -240,6 +242,65 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const char* __restric
   }
 }
 
+// The layer's last step when the down GEMM split its K loop: each live row of
+// y is first formed from its two fp32 partial planes exactly as
+// k_split_finish forms it (one fp32 add in plane order, one rounding) and
+// stored, then weighted into the token's output exactly as combine_kernel
+// does.  Every live row belongs to one (token, slot), so each is written once,
+// and y is not read back.
+template <class Tr>
+__global__ __launch_bounds__(kThreads) void combine_split_kernel(const float* __restrict__ part, size_t plane,
+                                                                 const float* __restrict__ topk_w,
+                                                                 const int32_t* __restrict__ row_of, int T, int k,
+                                                                 int d, char* __restrict__ y, char* __restrict__ out) {
+  using Elt = typename Tr::T;
+  constexpr int EPC = Tr::EPC;
+  const int t = blockIdx.x;
+  const size_t row_bytes = (size_t)d * sizeof(Elt);
+  const int nchunk = d / EPC;
+  for (int c = threadIdx.x; c < nchunk; c += kThreads) {
+    float acc[EPC];
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      float4 p0[4][EPC / 4], p1[4][EPC / 4];
+      float wj[4];
+      int row[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u;
+        row[u] = (j < k) ? row_of[(size_t)t * k + j] : -1;
+        wj[u] = row[u] >= 0 ? topk_w[(size_t)t * k + j] : 0.f;
+        const float* a = part + (size_t)(row[u] >= 0 ? row[u] : 0) * d + (size_t)c * EPC;
+#pragma unroll
+        for (int q = 0; q < EPC / 4; ++q) {
+          p0[u][q] = row[u] >= 0 ? *reinterpret_cast<const float4*>(a + 4 * q) : float4{0.f, 0.f, 0.f, 0.f};
+          p1[u][q] = row[u] >= 0 ? *reinterpret_cast<const float4*>(a + plane + 4 * q) : float4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (row[u] >= 0) {
+          float v[EPC];
+#pragma unroll
+          for (int q = 0; q < EPC / 4; ++q) {
+            v[4 * q] = p0[u][q].x + p1[u][q].x;
+            v[4 * q + 1] = p0[u][q].y + p1[u][q].y;
+            v[4 * q + 2] = p0[u][q].z + p1[u][q].z;
+            v[4 * q + 3] = p0[u][q].w + p1[u][q].w;
+          }
+          const uint4 ch = narrow<Tr>(v);
+          *reinterpret_cast<uint4*>(y + (size_t)row[u] * row_bytes + (size_t)c * 16) = ch;
+          widen<Tr>(ch, v);
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) acc[i] = fmaf(wj[u], v[i], acc[i]);
+        }
+      }
+    }
+    *reinterpret_cast<uint4*>(out + (size_t)t * row_bytes + (size_t)c * 16) = narrow<Tr>(acc);
+  }
+}
+
 // Sum of the two K ranges of the split down GEMM: one wavefront per row, fp32
 // planes added in plane order, one rounding to the element type.
 template <class Tr>
@@ -319,6 +380,18 @@ hipError_t launch_k_split_finish(int dtype, const float* part, size_t plane, con
   else
     hipLaunchKernelGGL(k_split_finish_kernel<TF32>, grid, block, 0, stream, part, plane, token_of, rows, N,
                        static_cast<char*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_split(int dtype, const float* part, size_t plane, const float* topk_w,
+                                const int32_t* row_of, int T, int k, int d, void* y, void* out, hipStream_t stream) {
+  const dim3 grid(T), block(kThreads);
+  if (dtype == 1)
+    hipLaunchKernelGGL(combine_split_kernel<TBF16>, grid, block, 0, stream, part, plane, topk_w, row_of, T, k, d,
+                       static_cast<char*>(y), static_cast<char*>(out));
+  else
+    hipLaunchKernelGGL(combine_split_kernel<TF32>, grid, block, 0, stream, part, plane, topk_w, row_of, T, k, d,
+                       static_cast<char*>(y), static_cast<char*>(out));
   return hipGetLastError();
 }
 

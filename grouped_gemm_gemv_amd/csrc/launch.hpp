@@ -110,6 +110,11 @@ struct GemmArgs {
 
 // y[r] = rounded(part[0][r] + part[1][r]) for every row r with token_of[r] >= 0:
 // the sum of the two K ranges of the split down GEMM, added in that order.
+// combine straight from the split down GEMM's fp32 planes part[2][R][d]
+// (plane = R*d floats): y rows formed as launch_k_split_finish forms them are
+// stored and weighted into out as launch_combine weights them.
+hipError_t launch_combine_split(int dtype, const float* part, size_t plane, const float* topk_w,
+                                const int32_t* row_of, int T, int k, int d, void* y, void* out, hipStream_t stream);
 hipError_t launch_k_split_finish(int dtype, const float* part, size_t plane, const int32_t* token_of, int64_t rows,
                                  int N, void* y, hipStream_t stream);
 

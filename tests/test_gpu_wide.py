@@ -154,3 +154,12 @@ def test_split_k_down(name):
     live = torch.from_numpy(np.nonzero(ref_disp["token_of"] >= 0)[0]).cuda()
     assert np.array_equal(bits(v.y_perm[live]), bits(y0[live]))
     assert np.array_equal(bits(out2), bits(out))
+    # moe_forward forms y inside its combine (combine_split_kernel); the
+    # separate steps (down GEMM + k_split_finish, then moe_combine) give the
+    # same y and the same output bits
+    M.moe_ffn_down(shape, v.h, wd, v.disp, ps, v.y_perm)
+    out3 = torch.empty_like(out)
+    M.moe_combine(shape, v.y_perm, w_d, v.disp, out3)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(v.y_perm[live]), bits(y0[live]))
+    assert np.array_equal(bits(out3), bits(out))
