@@ -127,6 +127,11 @@ def parse():
                          "fraction of the kernel's cycles, from PMC runs that together hold GRBM_GUI_ACTIVE, "
                          "TA_TA_BUSY_sum, TD_TD_BUSY_sum, TD_TC_STALL_sum, TCP_PENDING_STALL_CYCLES_sum, "
                          "TA_ADDR_STALLED_BY_TC_CYCLES_sum and SQ_VALU_MFMA_BUSY_CYCLES; then exit")
+    ap.add_argument("--loop-phases", action="store_true",
+                    help="run the workload's layer on libmoe_phases.so (the bf16 grouped GEMMs built with main-loop "
+                         "phase timing) and print, per GEMM, the share of each wavefront's loop cycles spent waiting "
+                         "for its loads, at the workgroup barrier, issuing activation loads + MFMAs, and issuing "
+                         "weight loads; then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print the grouped-GEMM HBM traffic from a FETCH_SIZE and a WRITE_SIZE run "
                          "(both with --pmc-calibration) and exit")
@@ -569,8 +574,86 @@ def cpu_baseline(wl, inp, sample_tokens):
                       f"{reps} run(s), {total:.1f} s, {cores} BLAS threads"}
 
 
+def loop_phases(args):
+    """Main-loop phase shares of the bf16 grouped GEMMs (see --loop-phases):
+    the layer runs on libmoe_phases.so, whose GEMM kernels are the product's
+    with shader-clock reads around each phase of every main-loop iteration."""
+    import ctypes
+
+    import torch
+
+    from grouped_gemm_gemv_amd import _lib
+    _lib.LIB_PATH = os.path.join(ROOT, "grouped_gemm_gemv_amd", "libmoe_phases.so")
+    import grouped_gemm_gemv_amd as M
+    from workloads import get_workload, make_inputs
+
+    wl = get_workload(args.workload)
+    if wl.dtype != "bf16":
+        print("--loop-phases times the bf16 GEMM kernels", file=sys.stderr)
+        sys.exit(2)
+    inp = make_inputs(wl, args.seed)
+
+    def dev(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    x, wr, bias = dev(inp.x), dev(inp.wr), dev(inp.bias)
+    wg, wu, wd = dev(inp.wg), dev(inp.wu), dev(inp.wd)
+    if args.weight_layout == "blocked16":
+        wg, wu, wd = M.moe_pack_blocked16(wg), M.moe_pack_blocked16(wu), M.moe_pack_blocked16(wd)
+    ids, w = dev(inp.topk_ids), dev(inp.topk_w)
+    shape = M.Shape(wl.T, wl.d, wl.E, wl.k, wl.F, wl.capacity, torch.bfloat16, 0,
+                    M.LAYOUT_BLOCKED16 if args.weight_layout == "blocked16" else M.LAYOUT_ROWS)
+    q = M.query(shape)
+    ws = M.workspace(q.forward_ws_bytes)
+    out = torch.empty((wl.T, wl.d), dtype=torch.bfloat16, device="cuda")
+    step = lambda: M.moe_forward(shape, x, wr, bias, ids, w, wg, wu, wd, out, ws)  # noqa: E731
+    v = step()
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    lib = _lib.lib()
+    slots = 1 << 17
+    buf = np.zeros(slots * 8, dtype=np.uint64)
+    ps = M.PASS_BOTH if q.n_passes == 2 else 0
+    print(f"# main-loop phases of the bf16 grouped GEMMs, workload {wl.name} (T={wl.T}, d={wl.d}, E={wl.E}, "
+          f"k={wl.k}, F={wl.F}), tile rows {q.tile_rows}, {args.weight_layout} weights; one launch each after "
+          f"{max(args.warmup, 1)} layers; shares of the summed loop cycles of every wavefront")
+    print("# gemm | wavefronts | iterations per wavefront | loop cycles per wavefront | wait for loads | barrier | "
+          "activation loads + MFMAs | weight loads | other")
+    for name, fn, reader in (
+            ("gate+up", lambda: M.moe_ffn_gate_up_gather(shape, x, wg, wu, v.disp, ps, v.h), lib.moe_loop_phases_gateup),
+            ("down", lambda: M.moe_ffn_down(shape, v.h, wd, v.disp, ps, v.y_perm), lib.moe_loop_phases_down)):
+        reader.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        reader.restype = ctypes.c_int
+        step()
+        torch.cuda.synchronize()
+        if reader(None, 1) != 0:
+            raise RuntimeError("clearing the phase buffer failed")
+        fn()
+        torch.cuda.synchronize()
+        if reader(buf.ctypes.data_as(ctypes.c_void_p), 0) != 0:
+            raise RuntimeError("reading the phase buffer failed")
+        r = buf.reshape(-1, 8)
+        r = r[r[:, 7] == 1].astype(np.float64)
+        if len(r) == 0:
+            print(f"{name} | 0 | - | - | (no WK = 1 main loop in this launch)")
+            continue
+        tot = r[:, 4].sum()
+        sh = r[:, :4].sum(axis=0) / tot
+        print(f"{name} | {len(r)} | {r[:, 5].mean():.1f} | {r[:, 4].mean():.0f} | {sh[0]:.3f} | {sh[1]:.3f} | "
+              f"{sh[2]:.3f} | {sh[3]:.3f} | {1 - sh.sum():.3f}", flush=True)
+
+
 def main():
     args = parse()
+    if args.loop_phases:
+        loop_phases(args)
+        return
     if args.summarize:
         summarize(args.summarize)
         return

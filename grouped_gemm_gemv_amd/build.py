@@ -1,5 +1,6 @@
-"""Build libmoe.so (the layer) and libmoe_peaks.so (measurement probes)
-in-tree with hipcc for gfx950.
+"""Build libmoe.so (the layer), libmoe_peaks.so (measurement probes) and
+libmoe_phases.so (the layer with main-loop phase timing in its bf16 grouped
+GEMMs, for measurement only) in-tree with hipcc for gfx950.
 
     python -m grouped_gemm_gemv_amd.build
 
@@ -22,11 +23,14 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 PEAKS_LIB = os.path.join(PKG, "libmoe_peaks.so")
+PHASES_LIB = os.path.join(PKG, "libmoe_phases.so")
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "gemm_bf16_gateup.hip", "gemm_bf16_down.hip",
            "gemm_f32_gateup.hip", "gemm_f32_down.hip", "gemm_fp8w_gateup.hip", "gemm_fp8w_down.hip", "layout.hip",
            "noalloc.hip"]
 PEAKS_SOURCES = ["peaks.hip"]
+# recompiled with MOE_LOOP_PHASES for libmoe_phases.so (the other objects are shared)
+PHASES_SOURCES = ["gemm_bf16_gateup.hip", "gemm_bf16_down.hip"]
 
 
 def hipcc() -> str:
@@ -42,9 +46,11 @@ def common_flags():
             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, phases = job
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ("_phases.o" if phases else ".o"))
+    cmd = [hipcc()] + common_flags() + (["-DMOE_LOOP_PHASES"] if phases else []) + \
+        ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -65,13 +71,14 @@ def _link(objs, lib: str) -> None:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
-    srcs = SOURCES + PEAKS_SOURCES
-    with ThreadPoolExecutor(len(srcs)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], PEAKS_LIB)
+    jobs = [(s, False) for s in SOURCES + PEAKS_SOURCES] + [(s, True) for s in PHASES_SOURCES]
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        objs = dict(zip(jobs, ex.map(_compile, jobs)))
+    _link([objs[(s, False)] for s in SOURCES], LIB)
+    _link([objs[(s, False)] for s in PEAKS_SOURCES], PEAKS_LIB)
+    _link([objs[(s, s in PHASES_SOURCES)] for s in SOURCES], PHASES_LIB)
     if verbose:
-        print(f"built {LIB} and {PEAKS_LIB}")
+        print(f"built {LIB}, {PEAKS_LIB} and {PHASES_LIB}")
     return LIB
 
 

@@ -78,6 +78,26 @@ namespace gemm {
 constexpr int kKB = 128;      // bytes of K per step
 constexpr int kXcdChunk = 8;  // units per chunk of the skewed workgroup-to-XCD mapping
 
+// Main-loop phase timing, compiled only into the measurement library
+// libmoe_phases.so (MOE_LOOP_PHASES): every wavefront of a WK = 1 loop sums the
+// shader-clock cycles it spends waiting for its loads, waiting at the
+// workgroup barrier, issuing the activation loads and MFMAs, and issuing the
+// weight loads, and stores the sums with its loop's total in g_loop_phases
+// (slot = workgroup * wavefronts + wavefront, modulo kPhaseSlots).  In the
+// product library phase_clock() is a constant and the sums fold away.
+constexpr int kPhaseSlots = 1 << 17;
+#ifdef MOE_LOOP_PHASES
+static __device__ unsigned long long g_loop_phases[kPhaseSlots * 8];
+__device__ __forceinline__ unsigned long long phase_clock() {
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  __builtin_amdgcn_sched_barrier(0);
+  return t;
+}
+#else
+__device__ __forceinline__ constexpr unsigned long long phase_clock() { return 0; }
+#endif
+
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time unroll).
 template <int N, int I = 0, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -298,20 +318,31 @@ struct Gemm {
     // The gate+up kernel raises the wavefront's issue priority while it issues
     // loads, so a wavefront busy with MFMAs on the same SIMD does not delay the
     // next loads (measured 1.5 % at 128 rows per expert; no gain for down).
+    [[maybe_unused]] unsigned long long ph_wait = 0, ph_bar = 0, ph_mma = 0, ph_wload = 0;
+    [[maybe_unused]] const unsigned long long ph_start = phase_clock();
     auto body = [&](int it, auto uc, auto waitc) {
       constexpr int u = decltype(uc)::value;
+      const unsigned long long t0 = phase_clock();
       wait_vm<decltype(waitc)::value>();
+      const unsigned long long t1 = phase_clock();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      const unsigned long long t2 = phase_clock();
       if constexpr (GATED) __builtin_amdgcn_s_setprio(2);
       load_a(it + PF, c.stage[(u + PF) % NA]);
       if constexpr (GATED) __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       if (WK == 1 || it * WK + c.wk < c.nk) compute(c.stage[u % NA], wq[u % NWS]);
       __builtin_amdgcn_sched_barrier(0);
+      const unsigned long long t3 = phase_clock();
       if constexpr (GATED) __builtin_amdgcn_s_setprio(2);
       load_w(it + PF, wq[(u + PF) % NWS]);
       if constexpr (GATED) __builtin_amdgcn_s_setprio(0);
+      const unsigned long long t4 = phase_clock();
+      ph_wait += t1 - t0;
+      ph_bar += t2 - t1;
+      ph_mma += t3 - t2;
+      ph_wload += t4 - t3;
     };
 
 #pragma unroll
@@ -340,6 +371,22 @@ struct Gemm {
     // LDS is reused or the wavefront ends
     wait_vm<0>();
     __syncthreads();
+#ifdef MOE_LOOP_PHASES
+    if constexpr (WK == 1) {
+      const unsigned slot = (blockIdx.x * NW + (threadIdx.x >> 6)) % kPhaseSlots;
+      if (lane == 0) {
+        unsigned long long* o = g_loop_phases + (size_t)slot * 8;
+        o[0] = ph_wait;
+        o[1] = ph_bar;
+        o[2] = ph_mma;
+        o[3] = ph_wload;
+        o[4] = phase_clock() - ph_start;
+        o[5] = c.nit;
+        o[6] = MS;
+        o[7] = 1;
+      }
+    }
+#endif
 
 
     if constexpr (WK > 1) {

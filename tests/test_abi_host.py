@@ -359,3 +359,25 @@ def test_probe_argument_checks_return_before_any_launch():
     assert lib.moe_peak_copy(fake, fake + 4096, 1024, 1, 7, None) == 1
     assert lib.moe_peak_mfma(1.0, 1.0, 0, fake, 1, None) == 1
     assert lib.moe_peak_mfma(1.0, 1.0, 1, None, 1, None) == 1
+
+
+# ---- measurement build (libmoe_phases) ----
+
+PHASES_HEADER = os.path.join(ROOT, "include", "moe_phases.h")
+PHASES_LIB = os.path.join(ROOT, "grouped_gemm_gemv_amd", "libmoe_phases.so")
+
+
+def test_phase_build_exports_the_layer_and_its_readers_only_there():
+    """libmoe_phases.so exports every moe.h symbol plus the two phase readers
+    of moe_phases.h; the product library libmoe.so has no phase reader."""
+    import ctypes
+    if not os.path.exists(PHASES_LIB):
+        pytest.skip("libmoe_phases.so not built")
+    readers = sorted(set(re.findall(r"^\s*int\s+(moe_\w+)\s*\(", open(PHASES_HEADER).read(), re.M)))
+    assert readers == ["moe_loop_phases_down", "moe_loop_phases_gateup"]
+    ph = ctypes.CDLL(PHASES_LIB)
+    for n in declared_functions() + readers:
+        assert hasattr(ph, n), n
+    prod = _lib.lib()
+    for n in readers:
+        assert not hasattr(prod, n), n
