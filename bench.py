@@ -127,6 +127,10 @@ def parse():
                          "fraction of the kernel's cycles, from PMC runs that together hold GRBM_GUI_ACTIVE, "
                          "TA_TA_BUSY_sum, TD_TD_BUSY_sum, TD_TC_STALL_sum, TCP_PENDING_STALL_CYCLES_sum, "
                          "TA_ADDR_STALLED_BY_TC_CYCLES_sum and SQ_VALU_MFMA_BUSY_CYCLES; then exit")
+    ap.add_argument("--cold-read", metavar="MB", default=None,
+                    help="comma-separated sizes: time one streaming read (libmoe_peaks) of each size right after a "
+                         "1 GiB read that evicts it from the caches, best over workgroup counts and cache policies "
+                         "(the single-launch ceiling of a GEMM that streams that many weight bytes); then exit")
     ap.add_argument("--loop-phases", action="store_true",
                     help="run the workload's layer on libmoe_phases.so (the bf16 grouped GEMMs built with main-loop "
                          "phase timing) and print, per GEMM, the share of each wavefront's loop cycles spent waiting "
@@ -649,8 +653,47 @@ def loop_phases(args):
               f"{sh[2]:.3f} | {sh[3]:.3f} | {1 - sh.sum():.3f}", flush=True)
 
 
+def cold_read(sizes_mb):
+    """Single-launch streaming-read ceilings at the given sizes: each timed
+    launch reads a buffer that a 1 GiB read just evicted from L2 and the
+    last-level cache, as a layer's GEMM finds its weights; median of 10
+    launches per (workgroups, cache policy), best of those."""
+    import torch
+
+    from grouped_gemm_gemv_amd import peaks as P
+    cur = torch.cuda.current_stream()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    print("# cold single-launch streaming read (libmoe_peaks moe_peak_read), each launch after a 1 GiB read; "
+          "median of 10 per setting, best setting")
+    print("# bytes | us | GB/s | workgroups | flags (1 non-temporal, 2 per-wavefront regions)")
+    for mb in sizes_mb:
+        nb = (int(mb * 1e6) // 65536) * 65536
+        buf = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(2)
+        best = None
+        for blk in (512, 1024, 2048, 4096):
+            for fl in range(4):
+                ts = []
+                for _ in range(10):
+                    P.moe_peak_read(flush, sink, 1024, 0)
+                    a, b = HipEvent(), HipEvent()
+                    a.record(cur)
+                    P.moe_peak_read(buf, sink, blk, fl)
+                    b.record(cur)
+                    b.synchronize()
+                    ts.append(a.elapsed_time(b) * 1e3)
+                t = float(np.median(ts))
+                if best is None or t < best[0]:
+                    best = (t, blk, fl)
+        print(f"{nb} | {best[0]:.1f} | {nb / best[0] / 1e3:.0f} | {best[1]} | {best[2]}", flush=True)
+        del buf
+
+
 def main():
     args = parse()
+    if args.cold_read:
+        cold_read([float(v) for v in args.cold_read.split(",")])
+        return
     if args.loop_phases:
         loop_phases(args)
         return

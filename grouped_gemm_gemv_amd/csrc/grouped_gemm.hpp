@@ -684,28 +684,26 @@ __global__ __launch_bounds__(64 * CN::WN) void grouped_gemm_wide_kernel(GemmArgs
     const int sm = map[t1 - 1].z <= CW::BM ? 1 : 0;
     return sm * NTw + (t1 - t0 - sm) * NTn;
   };
-  // per 64-expert chunk: units of each expert, their total and the skew test's
-  // tile statistics (as in grouped_gemm_kernel)
-  int total = 0, mx = 0, act = 0;
+  // total units over the experts, 64 at a time
+  int total = 0;
   for (int b = 0; b < p.E; b += 64) {
     const int i = b + lane;
-    const int u = i < p.E ? units_of(i) : 0;
-    const int t = i < p.E ? p.tile_off[i + 1] - p.tile_off[i] : 0;
-    int su = u;
+    int su = i < p.E ? units_of(i) : 0;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) su += __shfl_xor(su, o);
     total += su;
-    mx = max(mx, t);
-    act += __popcll(__ballot(t > 0));
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
   total = __builtin_amdgcn_readfirstlane(total);
-  mx = __builtin_amdgcn_readfirstlane(mx);
-  const bool skewed = p.skew_map && (long long)mx * act > 2LL * p.n_tiles[0];
+  // Units are always dealt to the XCDs in chunks of kXcdChunk consecutive
+  // units (with skew_map set): an expert with a tile of more than CW::BM rows
+  // has twice the units of the others, and contiguous per-XCD ranges would
+  // put them on one or two XCDs.  Measured at the Mixtral shape, T = 512,
+  // seeds 0 / 1 / 2 (seed 1 has one 149-row expert): gate+up 333 / 379 / 335
+  // against 335 / 407 / 344 us with contiguous ranges.
+  const bool chunked = p.skew_map != 0;
   const int j = blockIdx.x >> 3;
   int L;
-  if (!skewed) {
+  if (!chunked) {
     const int J = (total + 7) >> 3;
     if (j >= J) return;
     L = (blockIdx.x & 7) * J + j;
