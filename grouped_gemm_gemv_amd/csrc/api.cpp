@@ -347,11 +347,11 @@ moe::GemmArgs gemm_args(const moe_shape_t& s, const moe_dispatch_t& d, int pass,
 
 // Mean rows per expert for which the bf16 gate+up on the 160-row tile map
 // takes the two-width kernel (Wide160 in gemm_tiles.hpp).  Measured, 8
-// Mixtral experts: 3 % faster at 64 rows, 10 % at 128, 2 % slower at 32; and
-// 3 % slower when every expert holds 150-160 rows, where all tiles take the
-// one-width units: near a mean of 128 only the odd expert does.
+// Mixtral experts: 3 % faster at 64 rows, 10 % at 128, 13 % at 140-144,
+// 2-3 % faster even when every expert holds 148-160 rows (all of them in
+// 112-column units, dealt to the XCDs in chunks), 2 % slower at 32.
 constexpr int kWideMinRows = 48;
-constexpr int kWideMaxRows = 136;
+constexpr int kWideMaxRows = 160;
 
 
 // Gate+up over one pass.  With x_src set, activation row r is read from row
