@@ -57,6 +57,11 @@ int choose_tile_rows(const moe_shape_t& s) {
     // 8 experts of d = 3584: 64 rows 85 us at 160 vs 91 at 192, 192 rows 193 vs
     // 155 us; 8 Mixtral experts of 192 rows: 1001 vs 748 us; 32 or more
     // experts of d = 3584: 192 ahead by 2-7 %.
+    // 193-256 rows: two balanced 128-row tiles.  Measured per-expert cost
+    // curves, 224 / 256 rows: 8 Mixtral experts 775 / 813 us at 128 against
+    // 870 / 882 at 160 and 929 / 918 at 192; 32 experts of d = 2048,
+    // F = 1408: 173 / 181 us against 216 / 212 at 192.
+    if (mean > 192 && mean <= 256) return 128;
     const int64_t r192 = ceil_div(mean, 192);
     const int64_t w192 = active * r192 * ceil_div(s.d, 256);
     const bool past160 = w192 >= 112 && mean > 160 &&

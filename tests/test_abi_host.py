@@ -102,7 +102,10 @@ def test_automatic_tile_rows(name, bm):
     (256, 8, 2, 3584, 2560, 160),   # 224 tall down tiles >= 192; 8 x 14 tiles of 192 rows too few
     (1024, 32, 2, 3584, 2560, 192), # 32 x 14 = 448 tiles of 192 rows
     (1536, 8, 1, 3584, 2560, 192),  # 192 rows: one 192-row tile beats 160 + 32
-    (2048, 8, 1, 2048, 1408, 160),  # 256 rows: 2 x 160 pads less than 2 x 192
+    (2048, 8, 1, 2048, 1408, 128),  # 256 rows: two balanced 128-row tiles
+    (1792, 8, 1, 4096, 14336, 128), # 224 rows: two balanced 128-row tiles
+    (1600, 8, 1, 4096, 14336, 128), # 200 rows: 128 + 72 rather than 192 + 8
+    (1536, 8, 1, 4096, 14336, 192), # 192 rows: one 192-row tile
     (3584, 8, 1, 2048, 1408, 192),  # 448 rows, 8 x 3 x 8 tiles of 192 rows
     (8192, 8, 1, 2048, 1408, 384),  # 1024 rows per expert
     (4096, 1, 1, 4096, 14336, 384), # one expert of 4096 rows: 22 x 16 tiles of 192 rows, then 384
