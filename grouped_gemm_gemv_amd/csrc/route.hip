@@ -12,10 +12,12 @@
 // on the matrix cores (experts as MFMA rows, tokens as columns).  KW
 // wavefronts split K (64-byte slabs, wavefront w takes slabs w, w+KW, ...),
 // each issuing all loads of U slabs before its MFMAs; the KW partial tiles
-// are added in a fixed order through LDS (bitwise reproducible).  Top-k is
-// then k rounds of a wavefront-wide (value, index) argmax with cross-lane
-// shuffles, one token per wavefront at a time, one expert per lane (E <= 256
-// gives up to 4 per lane).
+// are added in a fixed order through LDS (bitwise reproducible).  Top-k, one
+// token per wavefront at a time: with E <= 64 (one expert per lane) each
+// expert's rank comes from one pass over the E logits (lane reads), and the
+// expert of rank j moves to lane j; past 64 experts (up to 4 per lane), k
+// rounds of a wavefront-wide (value, index) argmax with cross-lane shuffles.
+// Either way lane j ends with slot j.
 #include <float.h>
 
 #include "device_common.hpp"
@@ -111,7 +113,20 @@ __device__ void route_block(const typename Tr::T* __restrict__ x, const typename
     }
     int my_id = 0;
     float my_val = 0.f;
-    for (int j = 0; j < k; ++j) {
+    if (E <= 64) {
+      // one expert per lane: its rank is the number of experts ahead of it
+      // (larger logit, or an equal logit at a lower index); the expert of
+      // rank j is sent to lane j, which then holds slot j as below
+      int rank = 0;
+      for (int f = 0; f < E; ++f) {
+        const float vf = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[0]), f));
+        rank += (vf > v[0] || (vf == v[0] && f < lane)) ? 1 : 0;
+      }
+      const int dst = (lane < E ? rank : lane) * 4;  // a permutation of the 64 lanes
+      my_val = __builtin_bit_cast(float, __builtin_amdgcn_ds_permute(dst, __builtin_bit_cast(int, v[0])));
+      my_id = __builtin_amdgcn_ds_permute(dst, lane);
+    }
+    for (int j = 0; j < (E <= 64 ? 0 : k); ++j) {
       float bv = -FLT_MAX;
       int bi = 0x7fffffff;
 #pragma unroll
