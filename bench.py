@@ -628,7 +628,7 @@ def loop_phases(args):
           f"k={wl.k}, F={wl.F}), tile rows {q.tile_rows}, {args.weight_layout} weights; one launch each after "
           f"{max(args.warmup, 1)} layers; shares of the summed loop cycles of every wavefront")
     print("# gemm | wavefronts | iterations per wavefront | loop cycles per wavefront | wait for loads | barrier | "
-          "activation loads + MFMAs | weight loads | other")
+          "activation loads + MFMAs | weight loads | other | shader clock GHz over the loops")
     for name, fn, reader in (
             ("gate+up", lambda: M.moe_ffn_gate_up_gather(shape, x, wg, wu, v.disp, ps, v.h), lib.moe_loop_phases_gateup),
             ("down", lambda: M.moe_ffn_down(shape, v.h, wd, v.disp, ps, v.y_perm), lib.moe_loop_phases_down)):
@@ -649,8 +649,9 @@ def loop_phases(args):
             continue
         tot = r[:, 4].sum()
         sh = r[:, :4].sum(axis=0) / tot
+        ghz = tot / max(r[:, 6].sum(), 1.0) * 0.1  # cycles per 100 MHz tick / 10
         print(f"{name} | {len(r)} | {r[:, 5].mean():.1f} | {r[:, 4].mean():.0f} | {sh[0]:.3f} | {sh[1]:.3f} | "
-              f"{sh[2]:.3f} | {sh[3]:.3f} | {1 - sh.sum():.3f}", flush=True)
+              f"{sh[2]:.3f} | {sh[3]:.3f} | {1 - sh.sum():.3f} | {ghz:.2f}", flush=True)
 
 
 def cold_read(sizes_mb):

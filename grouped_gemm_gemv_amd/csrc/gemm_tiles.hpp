@@ -18,7 +18,7 @@
 
 namespace moe {
 
-template <int BM_, int WTN_, int WN_, int WK_, int PF_, int NTMS_ = 0, int RS_ = 1, int WS_ = 0>
+template <int BM_, int WTN_, int WN_, int WK_, int PF_, int NTMS_ = 0, int RS_ = 1, int WS_ = 0, int PP_ = 0>
 struct TileShape {
   static constexpr int BM = BM_, WTN = WTN_, WN = WN_, WK = WK_, PF = PF_;
   // A workgroup computes BM rows; a tile of the tile map (RS * BM rows) is
@@ -33,6 +33,9 @@ struct TileShape {
   // tiles of at most NTMS 16-row subtiles whose expert has one row tile load
   // the weights non-temporally
   static constexpr int NTMS = NTMS_;
+  // 1: the ping-pong main loop (the two wavefronts of each SIMD take turns at
+  // its matrix core, one phase apart; PF weight register sets and LDS stages)
+  static constexpr int PP = PP_;
 };
 
 // WQ: E4M3 weight codes; they take the bf16 shapes unless specialised below.
@@ -51,7 +54,7 @@ template <> struct TileCfg<64, true> { using type = TileShape<64, 16, 4, 2, 4, 4
 template <> struct TileCfg<96, true> { using type = TileShape<96, 16, 8, 1, 4, 4>; };
 template <> struct TileCfg<128, true> { using type = TileShape<128, 16, 8, 1, 4, 4>; };
 template <> struct TileCfg<160, true> { using type = TileShape<160, 16, 7, 1, 4, 4>; };
-template <> struct TileCfg<192, true> { using type = TileShape<192, 16, 8, 1, 4, 4>; };
+template <> struct TileCfg<192, true> { using type = TileShape<192, 16, 8, 1, 4, 4, 1, 0, 1>; };
 // E4M3 gate+up at BM 160 (T = 512 at the Mixtral shape): the matrix cores,
 // not HBM, set its time, and with half the weight registers of bf16 the
 // 32-row shape fits at 160 rows in the register-lean form; each activation
@@ -60,7 +63,10 @@ template <> struct TileCfg<160, true, true> { using type = TileShape<160, 32, 8,
 // BM 384 (compute-heavy shapes): the 384-row tiles of the tile map are worked
 // in three 128-row pieces with 32 weight rows per wavefront, so each
 // activation fragment read from LDS feeds four MFMAs (two at BM 192).
-template <> struct TileCfg<384, true> { using type = TileShape<128, 32, 8, 1, 2, 4, 3>; };
+// BM 192 and 384 take the ping-pong main loop: measured against the shared
+// loop, gate+up 1605 vs 1718 us at T = 4096 (Mixtral shape) and 311 vs 343
+// us in the capacity workload at Gini 0.10; unchanged on the 64-expert shape.
+template <> struct TileCfg<384, true> { using type = TileShape<128, 32, 8, 1, 2, 4, 3, 0, 1>; };
 
 // bf16 gate+up on the 160-row tile map, from about 48 rows per expert (one
 // launch of grouped_gemm_wide_kernel): tiles of at most 144 rows in 224-column
@@ -103,7 +109,10 @@ template <> struct TileCfg<160, false, true> { using type = TileShape<160, 32, 4
 // moved into LDS feeds twice the weight bytes.
 using Split160 = TileShape<160, 32, 8, 1, 4, 10>;
 
-// BM 384: two 192-row pieces, the BM 192 shape.
-template <> struct TileCfg<384, false> { using type = TileShape<192, 32, 8, 1, 2, 4, 2>; };
+// BM 384: two 192-row pieces, the BM 192 shape, with the ping-pong main loop
+// (T = 4096: down 793 vs 846 us).  The 192-row tiles of the map itself keep
+// the shared loop: with the ping-pong loop they ran 1-3 % slower where
+// experts hold 70-400 rows (64-expert and capacity workloads).
+template <> struct TileCfg<384, false> { using type = TileShape<192, 32, 8, 1, 2, 4, 2, 0, 1>; };
 
 }  // namespace moe

@@ -82,7 +82,9 @@ constexpr int kXcdChunk = 8;  // units per chunk of the skewed workgroup-to-XCD 
 // libmoe_phases.so (MOE_LOOP_PHASES): every wavefront of a WK = 1 loop sums the
 // shader-clock cycles it spends waiting for its loads, waiting at the
 // workgroup barrier, issuing the activation loads and MFMAs, and issuing the
-// weight loads, and stores the sums with its loop's total in g_loop_phases
+// weight loads (ping-pong loop: waits, barriers, MFMA phases, load issue and
+// LDS fragment reads), and stores the sums with its loop's total and the
+// loop's duration on the constant 100 MHz counter in g_loop_phases
 // (slot = workgroup * wavefronts + wavefront, modulo kPhaseSlots).  In the
 // product library phase_clock() is a constant and the sums fold away.
 constexpr int kPhaseSlots = 1 << 17;
@@ -94,8 +96,11 @@ __device__ __forceinline__ unsigned long long phase_clock() {
   __builtin_amdgcn_sched_barrier(0);
   return t;
 }
+// the constant 100 MHz counter, to turn loop cycles into the shader clock rate
+__device__ __forceinline__ unsigned long long phase_realtime() { return __builtin_amdgcn_s_memrealtime(); }
 #else
 __device__ __forceinline__ constexpr unsigned long long phase_clock() { return 0; }
+__device__ __forceinline__ constexpr unsigned long long phase_realtime() { return 0; }
 #endif
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time unroll).
@@ -126,7 +131,8 @@ __device__ __forceinline__ uint4 widen_e4m3(unsigned lo, unsigned hi) {
 // KS workgroups (KS = 1 or 2).  With KS = 2 each workgroup stores its fp32
 // partial sums, unrounded, in plane ks of a [2][R][N] buffer, and a separate
 // kernel adds the two planes (k_split_finish): no workgroup waits for another.
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int WS = 0, int KS = 1>
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int WS = 0, int KS = 1,
+          int PP = 0>
 struct Gemm {
   using Elt = typename Tr::T;
   static_assert(!WQ || std::is_same<Tr, TBF16>::value, "fp8 weights take bf16 activations");
@@ -186,6 +192,85 @@ struct Gemm {
   // reads the same weights (see run_ms).
   static constexpr int kNonTemporal = 2;
 
+  // Source and LDS offsets of this wavefront's QW LDS-direct loads of an
+  // activation stage of NQ 1 KB instructions (instruction q = wave + i * NW,
+  // the last ones repeating instruction NQ - 1): 16-byte slot pos = 64 q +
+  // lane holds chunk g of row r (swizzled); rows past the tile's last read
+  // from an offset past the buffer's bound, so they load zeros.
+  template <int NQ, int QW>
+  __device__ __forceinline__ static void act_plan(const Ctx& c, int wave, int lane, int (&aoff)[QW], int (&lofs)[QW]) {
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+      const int q = min(wave + i * NW, NQ - 1);
+      const int pos = q * 64 + lane;            // 16-byte slot in the stage
+      const int r = pos / CPR;
+      const int pc = pos - r * CPR;
+      const int g = (pc & ~7) | ((pc & 7) ^ swz(r));  // chunk of the row this slot holds
+      const int src = (r < c.rows) ? (c.arow != nullptr ? c.arow[r] : r) : -1;
+      aoff[i] = (src >= 0) ? src * c.ld + g * 16 : 0x7ff00000;
+      lofs[i] = q * 1024;
+    }
+  }
+
+  // Weight loads of iteration `it` into one register set (WL 16-byte loads per
+  // lane); past the last iteration the K step is clamped and the values go
+  // unused.  bf16: per subtile, the two 16-byte halves of the lane's chunk of
+  // the 128-byte step; E4M3: one 16-byte load holds the lane's codes of both
+  // K halves.
+  template <int WAUX>
+  __device__ __forceinline__ static void load_w_step(const Ctx& c, int it, uint4* dst) {
+    const int s = c.s0 + min(it * WK + c.wk, c.nk - 1);
+    if constexpr (WQ) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i)
+          dst[m * NSUB + i] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * c.wstep, WAUX));
+    } else {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            dst[(m * NSUB + i) * 2 + h] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * c.wstep + h * c.whalf, WAUX));
+    }
+  }
+
+  // The weight loads of iteration `it` that fill half h of a register set
+  // (bf16: the 16-byte pieces of K half h of every subtile; E4M3: every load
+  // for h = 1, none for h = 0, since one load holds both K halves).
+  template <int WAUX>
+  __device__ __forceinline__ static void load_w_half(const Ctx& c, int it, uint4* dst, int h) {
+    const int s = c.s0 + min(it * WK + c.wk, c.nk - 1);
+    if constexpr (WQ) {
+      if (h == 1) load_w_step<WAUX>(c, it, dst);
+    } else {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i)
+          dst[(m * NSUB + i) * 2 + h] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * c.wstep + h * c.whalf, WAUX));
+    }
+  }
+
+  // This wavefront's qw LDS-direct loads of the activation tile of iteration
+  // `it` into stage `st` (aoff: source byte offsets, lofs: LDS offsets);
+  // iterations past the last are clamped to it.  (qw is a constant at every
+  // call; the loop unrolls once inlined.)
+  __device__ __forceinline__ static void load_a_step(const Ctx& c, int it, char* st, const int* aoff,
+                                                     const int* lofs, int qw) {
+    const int itc = min(it, c.nit - 1);
+#pragma unroll
+    for (int i = 0; i < qw; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          c.act, (__attribute__((address_space(3))) void*)(st + lofs[i]), 16, aoff[i] + itc * ROWB + c.s0 * kKB,
+          0, 0, 0);
+  }
+
   template <int MS, int WAUX>
   __device__ __forceinline__ static void run(const Ctx& c) {
     // The activation tile of an iteration (MS*16 rows x ROWB bytes) is moved
@@ -202,17 +287,7 @@ struct Gemm {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int aoff[QW];
     int lofs[QW];
-#pragma unroll
-    for (int i = 0; i < QW; ++i) {
-      const int q = min(wave + i * NW, NQ - 1);
-      const int pos = q * 64 + lane;            // 16-byte slot in the stage
-      const int r = pos / CPR;
-      const int pc = pos - r * CPR;
-      const int g = (pc & ~7) | ((pc & 7) ^ swz(r));  // chunk of the row this slot holds
-      const int src = (r < c.rows) ? (c.arow != nullptr ? c.arow[r] : r) : -1;
-      aoff[i] = (src >= 0) ? src * c.ld + g * 16 : 0x7ff00000;
-      lofs[i] = q * 1024;
-    }
+    act_plan<NQ, QW>(c, wave, lane, aoff, lofs);
     // reader: row jm*16 + lane%16; swz of that row depends on the lane only
     const int rd = (lane & 15) * ROWB + c.wk * kKB;
     const int rsw = swz(lane & 15);
@@ -227,37 +302,8 @@ struct Gemm {
 
     uint4 wq[NWS][WL];
 
-    auto load_w = [&](int it, uint4* dst) {
-      const int s = c.s0 + min(it * WK + c.wk, c.nk - 1);  // clamped: values past the end are unused
-      if constexpr (WQ) {
-        // one 16-byte load holds this lane's codes of both K halves
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int i = 0; i < NSUB; ++i)
-            dst[m * NSUB + i] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * c.wstep, WAUX));
-      } else {
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int i = 0; i < NSUB; ++i)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              dst[(m * NSUB + i) * 2 + h] = __builtin_bit_cast(
-                  uint4, __builtin_amdgcn_raw_buffer_load_b128(c.w[m], c.wlane[i], s * c.wstep + h * c.whalf, WAUX));
-      }
-    };
-    // activation tile of iteration `it` into LDS stage `st`; past the last
-    // iteration the loads are clamped and their data is never read
-    auto load_a = [&](int it, char* st) {
-      const int itc = min(it, c.nit - 1);
-#pragma unroll
-      for (int i = 0; i < QW; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            c.act, (__attribute__((address_space(3))) void*)(st + lofs[i]), 16, aoff[i] + itc * ROWB + c.s0 * kKB,
-            0, 0, 0);
-    };
+    auto load_w = [&](int it, uint4* dst) { load_w_step<WAUX>(c, it, dst); };
+    auto load_a = [&](int it, char* st) { load_a_step(c, it, st, aoff, lofs, QW); };
     // MFMA operands of one step, half h (32 of its 64 K elements).  bf16
     // weights: lane group g = lane/16 holds elements 32h + 8g .. +7 of both
     // operands.  fp8 weights: a lane's 16 codes are elements 16g .. 16g+15,
@@ -319,7 +365,7 @@ struct Gemm {
     // loads, so a wavefront busy with MFMAs on the same SIMD does not delay the
     // next loads (measured 1.5 % at 128 rows per expert; no gain for down).
     [[maybe_unused]] unsigned long long ph_wait = 0, ph_bar = 0, ph_mma = 0, ph_wload = 0;
-    [[maybe_unused]] const unsigned long long ph_start = phase_clock();
+    [[maybe_unused]] const unsigned long long ph_start = phase_clock(), ph_rt = phase_realtime();
     auto body = [&](int it, auto uc, auto waitc) {
       constexpr int u = decltype(uc)::value;
       const unsigned long long t0 = phase_clock();
@@ -382,7 +428,7 @@ struct Gemm {
         o[3] = ph_wload;
         o[4] = phase_clock() - ph_start;
         o[5] = c.nit;
-        o[6] = MS;
+        o[6] = phase_realtime() - ph_rt;
         o[7] = 1;
       }
     }
@@ -429,8 +475,211 @@ struct Gemm {
       if (c.wk != 0) return;
     }
 
-    // epilogue: lane holds rows n = n0 + 16 i + 4 (lane/16) + r of column m
-    // (fp8 weights: times the scale of channel n)
+    store_tile<MS>(c, acc);
+  }
+
+  // Ping-pong main loop (PP): the two wavefronts that share a SIMD (wave w
+  // and w + NW/2: gfx950 places the wavefronts of a workgroup on the SIMDs
+  // with period 4) take turns at its matrix core, so that one issues MFMAs
+  // while the other waits for memory, issues loads and reads its next
+  // operands from LDS.  Each half step (32 K elements) of an iteration is
+  // one MFMA phase; phases are separated by workgroup barriers, and the
+  // second group of wavefronts runs one phase behind the first.  Per
+  // iteration i (stage and weight register set i mod PF), a wavefront runs
+  //   MFMA(i, half 0)                       [operands already in registers]
+  //   MEM0: issue iteration i + PF's weights for K half 0 (into the half of
+  //         the set just multiplied); read half 1's activation fragments of
+  //         stage i; wait until its own loads of iteration i + 1's
+  //         activations have landed
+  //   MFMA(i, half 1)
+  //   MEM1: issue iteration i + PF's weights for K half 1 and its activation
+  //         tile (into stage i mod PF, whose fragments every wavefront has
+  //         read: each reads them before a barrier that precedes this phase,
+  //         and waits for the reads); read half 0's fragments of stage i + 1
+  //         (landed: every wavefront waited for its part in its MEM0 before a
+  //         barrier that precedes this phase); wait until its weights of
+  //         iteration i + 1 for half 0 have landed (half 1's are covered by
+  //         the next MEM0's wait, since they were issued before the
+  //         activations it waits for)
+  // with a barrier after each of the four.  The second group adds one barrier
+  // before the loop and the first one after it, so every wavefront passes
+  // the same number of barriers.  Each wavefront waits for its LDS reads
+  // before the barrier that ends a memory phase, so its MFMA phase needs no
+  // wait.  Splitting the weight loads over both memory phases keeps each
+  // phase's burst of loads (four wavefronts of a compute unit issue at once)
+  // within what the compute unit's load path moves during an MFMA phase.
+  // The activation fragments of one half step are the only operand registers
+  // beyond the weight sets, so the tile fits in the registers of two
+  // wavefronts per SIMD.
+  template <int MS, int WAUX>
+  __device__ __forceinline__ static void run_pp(const Ctx& c) {
+    static_assert(WK == 1 && NW % 2 == 0 && PF >= 2, "ping-pong shape");
+    constexpr int NQ = MS * 16 * CPR / 64;
+    constexpr int QW = (NQ + NW - 1) / NW;
+    // loads per iteration: W0 weight loads in MEM0 (K half 0 of the set just
+    // multiplied), then W1 weight loads and the QW activation loads in MEM1
+    constexpr int W0 = WQ ? 0 : WL / 2, W1 = WL - W0, L = WL + QW;
+    constexpr int WAIT_A = W0 + (PF - 2) * L;       // MEM0: activations of i + 1 landed
+    constexpr int WAIT_W = W1 + QW + (PF - 1) * L;  // MEM1: weights of i + 1 for half 0 landed
+    constexpr int WAIT_0 = (PF - 1) * L;            // prologue: iteration 0 landed
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool second = wave >= NW / 2;
+    int aoff[QW];
+    int lofs[QW];
+    act_plan<NQ, QW>(c, wave, lane, aoff, lofs);
+    const int rd = (lane & 15) * ROWB;
+    const int rsw = swz(lane & 15);
+
+    f32x4_t acc[NMAT][NSUB][MS];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+        for (int jm = 0; jm < MS; ++jm) acc[m][i][jm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 wq[PF][WL];
+    uint4 af[MS];
+    auto load_w = [&](int it, uint4* dst, int h) { load_w_half<WAUX>(c, it, dst, h); };
+    auto load_a = [&](int it, char* st) { load_a_step(c, it, st, aoff, lofs, QW); };
+
+    auto barrier = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // activation fragments of half h from stage st (same K order as `run`)
+    auto read_frags = [&](const char* st, int h) {
+      const int chunk = WQ ? 2 * (lane >> 4) + h : h * 4 + (lane >> 4);
+      const char* lb = st + rd + (chunk ^ rsw) * 16;
+#pragma unroll
+      for (int jm = 0; jm < MS; ++jm) af[jm] = *reinterpret_cast<const uint4*>(lb + jm * 16 * ROWB);
+    };
+    auto wait_lds = [&]() { __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8)); };
+    auto mfma_half = [&](const uint4* w, int h) {
+      uint4 wop[NMAT * NSUB];
+#pragma unroll
+      for (int q = 0; q < NMAT * NSUB; ++q) {
+        if constexpr (WQ)
+          wop[q] = h == 0 ? widen_e4m3(w[q].x, w[q].y) : widen_e4m3(w[q].z, w[q].w);
+        else
+          wop[q] = w[q * 2 + h];
+      }
+#pragma unroll
+      for (int jm = 0; jm < MS; ++jm)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int i = 0; i < NSUB; ++i) acc[m][i][jm] = mma16<Tr>(wop[m * NSUB + i], af[jm], acc[m][i][jm]);
+    };
+    // One iteration.  In the main loop every iteration issues the loads of
+    // iteration it + PF (clamped past the last, so the counts of the waits
+    // hold).  TAIL: one of the last nit mod PF iterations, which issues no
+    // loads (they would be for iterations past the last); what it still has
+    // to wait for was issued in the main loop, so it waits for all of that.
+    // phase sums (measurement build only): waits for loads and LDS reads,
+    // barriers, MFMA phases, load issue and fragment reads
+    [[maybe_unused]] unsigned long long ph_wait = 0, ph_bar = 0, ph_mma = 0, ph_issue = 0;
+    [[maybe_unused]] const unsigned long long ph_start = phase_clock(), ph_rt = phase_realtime();
+    auto tbar = [&]() {
+      const unsigned long long t = phase_clock();
+      barrier();
+      ph_bar += phase_clock() - t;
+    };
+    auto body = [&](int it, auto uc, auto tailc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr bool TAIL = decltype(tailc)::value;
+      unsigned long long t = phase_clock();
+      mfma_half(wq[u], 0);
+      ph_mma += phase_clock() - t;
+      tbar();
+      t = phase_clock();
+      if constexpr (!TAIL) load_w(it + PF, wq[u], 0);
+      read_frags(c.stage[u], 1);
+      ph_issue += phase_clock() - t;
+      t = phase_clock();
+      if constexpr (TAIL) {
+        if (it + 1 < c.nit) wait_vm<0>();
+      } else {
+        wait_vm<WAIT_A>();
+      }
+      wait_lds();
+      ph_wait += phase_clock() - t;
+      tbar();
+      t = phase_clock();
+      mfma_half(wq[u], 1);
+      ph_mma += phase_clock() - t;
+      tbar();
+      t = phase_clock();
+      if constexpr (!TAIL) {
+        load_w(it + PF, wq[u], 1);
+        load_a(it + PF, c.stage[u]);
+      }
+      read_frags(c.stage[(u + 1) % PF], 0);
+      ph_issue += phase_clock() - t;
+      t = phase_clock();
+      if constexpr (TAIL) {
+        if (it + 1 < c.nit) wait_vm<0>();
+      } else {
+        wait_vm<WAIT_W>();
+      }
+      wait_lds();
+      ph_wait += phase_clock() - t;
+      tbar();
+    };
+
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      load_w(u, wq[u], 0);
+      load_w(u, wq[u], 1);
+      load_a(u, c.stage[u]);
+    }
+    wait_vm<WAIT_0>();
+    barrier();
+    read_frags(c.stage[0], 0);
+    wait_lds();
+    if (second) barrier();
+    // whole rounds of PF iterations with no run-time test inside (the wait
+    // counts the compiler derives then match the explicit ones), then the
+    // rest; an iteration past the last is skipped by every wavefront alike,
+    // its barriers with it
+    int it0 = 0;
+    for (; it0 + PF <= c.nit; it0 += PF)
+      static_for<PF>([&](auto uc) { body(it0 + decltype(uc)::value, uc, std::false_type{}); });
+    static_for<PF - 1>([&](auto uc) {
+      if (it0 + decltype(uc)::value < c.nit) body(it0 + decltype(uc)::value, uc, std::true_type{});
+    });
+    if (!second) barrier();
+    // the trailing (clamped) loads still write LDS: drain them before the
+    // LDS is reused or the wavefront ends
+    wait_vm<0>();
+    __syncthreads();
+#ifdef MOE_LOOP_PHASES
+    {
+      const unsigned slot = (blockIdx.x * NW + wave) % kPhaseSlots;
+      if (lane == 0) {
+        unsigned long long* o = g_loop_phases + (size_t)slot * 8;
+        o[0] = ph_wait;
+        o[1] = ph_bar;
+        o[2] = ph_mma;
+        o[3] = ph_issue;
+        o[4] = phase_clock() - ph_start;
+        o[5] = c.nit;
+        o[6] = phase_realtime() - ph_rt;
+        o[7] = 1;
+      }
+    }
+#endif
+    store_tile<MS>(c, acc);
+  }
+
+  // Epilogue of a workgroup's tile: lane holds rows n = n0 + 16 i + 4 (lane/16)
+  // + r of column m (fp8 weights: times the scale of channel n); gate+up
+  // stores silu(gate) * up, down the sum (fp32 partial sums with the K split).
+  template <int MS>
+  __device__ __forceinline__ static void store_tile(const Ctx& c, const f32x4_t (&acc)[NMAT][NSUB][MS]) {
+    const int lane = threadIdx.x & 63;
     float sc[NMAT][NSUB][4];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
@@ -473,17 +722,25 @@ struct Gemm {
   // Main loop for exactly ms subtiles.  `once`: the expert has a single row
   // tile in this launch, so each weight byte is read by one workgroup only;
   // tiles of at most NTMS subtiles then load the weights non-temporally.
+  template <int M, int WAUX>
+  __device__ __forceinline__ static void go(const Ctx& c) {
+    if constexpr (PP)
+      run_pp<M, WAUX>(c);
+    else
+      run<M, WAUX>(c);
+  }
+
   template <int M>
   __device__ __forceinline__ static void run_ms(int ms, bool once, const Ctx& c) {
     if constexpr (M >= 1) {
       if (ms == M) {
         if constexpr (M <= NTMS) {
           if (once) {
-            run<M, kNonTemporal>(c);
+            go<M, kNonTemporal>(c);
             return;
           }
         }
-        run<M, 0>(c);
+        go<M, 0>(c);
         return;
       }
       run_ms<M - 1>(ms, once, c);
@@ -544,9 +801,10 @@ __device__ __forceinline__ void setup_ctx(typename G::Ctx& c, const GemmArgs& p,
   }
 }
 
-template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int RS, int WS, int KS>
+template <class Tr, int BM, int WTN, int WN, int WK, bool GATED, int PF, int NTMS, bool WQ, int RS, int WS, int KS,
+          int PP>
 __global__ __launch_bounds__(64 * WN * WK) void grouped_gemm_kernel(GemmArgs p) {
-  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, NTMS, WQ, WS, KS>;
+  using G = Gemm<Tr, BM, WTN, WN, WK, GATED, PF, NTMS, WQ, WS, KS, PP>;
   // one LDS array per activation stage (stages past NA are 16-byte stubs)
   __shared__ __attribute__((aligned(16))) char st0[G::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[G::STAGE];
@@ -781,7 +1039,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const long long grid = ((units + round - 1) / round) * round;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((grouped_gemm_kernel<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, GATED, Cfg::PF, Cfg::NTMS, WQ, Cfg::RS,
-                                         Cfg::WS, KS>),
+                                         Cfg::WS, KS, Cfg::PP>),
                      dim3((unsigned)grid), dim3(64 * Cfg::WN * Cfg::WK), 0, stream, a);
   return hipGetLastError();
 }

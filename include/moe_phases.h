@@ -10,8 +10,12 @@
  *   [2] issuing the activation loads and its MFMAs (including the LDS reads
  *       of the activation fragments and any wait for the matrix core),
  *   [3] issuing its weight loads,
- * followed by [4] the cycles of the whole loop, [5] its iterations, [6] the
- * 16-row subtiles of its tile and [7] = 1, as 8 uint64 per slot.  Slot =
+ * (in the ping-pong main loop of the compute-heavy tiles: [0] waits for its
+ * loads and LDS reads, [1] barriers, [2] its MFMA phases, [3] issuing its
+ * loads and LDS fragment reads), followed by [4] the cycles of the whole
+ * loop, [5] its iterations, [6] the loop's duration in ticks of the constant
+ * 100 MHz counter (so [4] / [6] * 100 MHz is the shader clock over the loop)
+ * and [7] = 1, as 8 uint64 per slot.  Slot =
  * (workgroup id * wavefronts per workgroup + wavefront) modulo
  * MOE_PHASE_SLOTS.  Only main loops without a K split inside the workgroup
  * (tiles of 96 rows and more) record.  It is for measuring where a GEMM's
