@@ -110,9 +110,10 @@ template <> struct TileCfg<160, false, true> { using type = TileShape<160, 32, 4
 using Split160 = TileShape<160, 32, 8, 1, 4, 10>;
 
 // BM 384: two 192-row pieces, the BM 192 shape, with the ping-pong main loop
-// (T = 4096: down 793 vs 846 us).  The 192-row tiles of the map itself keep
+// and prefetch depth 3 (T = 4096: down 793 vs 846 us with depth 2, 772 vs
+// 809 us for depth 3 against 2).  The 192-row tiles of the map itself keep
 // the shared loop: with the ping-pong loop they ran 1-3 % slower where
 // experts hold 70-400 rows (64-expert and capacity workloads).
-template <> struct TileCfg<384, false> { using type = TileShape<192, 32, 8, 1, 2, 4, 2, 0, 1>; };
+template <> struct TileCfg<384, false> { using type = TileShape<192, 32, 8, 1, 3, 4, 2, 0, 1>; };
 
 }  // namespace moe
