@@ -67,14 +67,20 @@ int choose_tile_rows(const moe_shape_t& s) {
     const bool past160 = w192 >= 112 && mean > 160 &&
                          (mean > 320 || r192 * 192 <= ceil_div(mean, 160) * 160);
     if (!(w192 >= 448 || past160)) return 160;
-    // A thousand rows or more per expert: 384-row tiles, which gate+up works
-    // in 128-row pieces with 32 weight rows per wavefront (twice the MFMAs
-    // per activation fragment read from LDS) and down in 192-row pieces.
-    // Mixtral, 8 experts of 1024 rows: 2590 vs 2826 us; with fewer rows the
-    // gain is uneven (8 experts of d = 2048 at 768 rows: 149 vs 139 us), and
-    // experts shorter than a tile leave pieces empty, whose workgroups still
-    // hold a compute unit while they find that out.
-    return mean >= 1024 ? 384 : 192;
+    // A thousand rows or more per expert, or past 384 rows with large experts
+    // (d * F of 2^25 or more): 384-row tiles, which gate+up works in 128-row
+    // pieces with 32 weight rows per wavefront (twice the MFMAs per
+    // activation fragment read from LDS) and down in 192-row pieces, both
+    // with the ping-pong main loop.  Per-expert cost curves with these
+    // kernels: 8 Mixtral experts (d * F = 58.7M) of 448 / 512 / 640 / 768
+    // rows 1268 / 1321 / 1696 / 1817 us against 1406 / 1461 / 1733 / 1864 at
+    // 192, of 384 rows 1024 against 1012; 32 experts of d = 2048, F = 1408
+    // ahead at 192 up to 768 rows (448 rows: 303 vs 313 us) and behind at
+    // 1024 (629 vs 580 us); 32 experts of d = 3584, F = 2560 within 2 % at
+    // 448-768 rows.  Experts shorter than a tile leave pieces empty, whose
+    // workgroups still hold a compute unit while they find that out.
+    const bool large = (int64_t)s.d * s.F >= (int64_t(1) << 25);
+    return (mean >= 1024 || (large && mean > 384)) ? 384 : 192;
   }
   if (mean > 32) return 64;
   if (active * ceil_div(s.d, 64) >= kComputeUnits) return 48;

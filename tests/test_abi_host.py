@@ -108,6 +108,10 @@ def test_automatic_tile_rows(name, bm):
     (1536, 8, 1, 4096, 14336, 192), # 192 rows: one 192-row tile
     (3584, 8, 1, 2048, 1408, 192),  # 448 rows, 8 x 3 x 8 tiles of 192 rows
     (8192, 8, 1, 2048, 1408, 384),  # 1024 rows per expert
+    (3584, 8, 1, 4096, 14336, 384), # 448 rows of large experts (d * F >= 2^25): 384-row tiles
+    (3072, 8, 1, 4096, 14336, 192), # 384 rows of large experts: two 192-row tiles
+    (6144, 8, 1, 4096, 14336, 384), # 768 rows of large experts
+    (24576, 32, 1, 3584, 2560, 192),# 768 rows of d * F = 9.2M: 192
     (4096, 1, 1, 4096, 14336, 384), # one expert of 4096 rows: 22 x 16 tiles of 192 rows, then 384
 ])
 def test_tile_rows_rule_shapes(T, E, k, d, F, bm):
