@@ -54,7 +54,7 @@ template <> struct TileCfg<64, true> { using type = TileShape<64, 16, 4, 2, 4, 4
 template <> struct TileCfg<96, true> { using type = TileShape<96, 16, 8, 1, 4, 4>; };
 template <> struct TileCfg<128, true> { using type = TileShape<128, 16, 8, 1, 4, 4>; };
 template <> struct TileCfg<160, true> { using type = TileShape<160, 16, 7, 1, 4, 4>; };
-template <> struct TileCfg<192, true> { using type = TileShape<192, 16, 8, 1, 4, 4, 1, 0, 1>; };
+template <> struct TileCfg<192, true> { using type = TileShape<192, 16, 8, 1, 3, 4, 1, 0, 1>; };
 // E4M3 gate+up at BM 160 (T = 512 at the Mixtral shape): the matrix cores,
 // not HBM, set its time, and with half the weight registers of bf16 the
 // 32-row shape fits at 160 rows in the register-lean form; each activation
@@ -66,6 +66,10 @@ template <> struct TileCfg<160, true, true> { using type = TileShape<160, 32, 8,
 // BM 192 and 384 take the ping-pong main loop: measured against the shared
 // loop, gate+up 1605 vs 1718 us at T = 4096 (Mixtral shape) and 311 vs 343
 // us in the capacity workload at Gini 0.10; unchanged on the 64-expert shape.
+// At BM 192 prefetch depth 3 (3 weight register sets and LDS stages in the
+// ping-pong loop) against 4: capacity Gini 0.10 / 0.30 302 / 321 vs 311 /
+// 332 us, 64 experts at Zipf 0 / 2.0 397 / 429 vs 404 / 436 us; depth 2 no
+// faster than 4.
 template <> struct TileCfg<384, true> { using type = TileShape<128, 32, 8, 1, 2, 4, 3, 0, 1>; };
 
 // bf16 gate+up on the 160-row tile map, from about 48 rows per expert (one

@@ -1,5 +1,5 @@
 """GPU parity of the ping-pong main loop of the grouped GEMMs (bf16): gate+up
-on 192- and 384-row tiles (prefetch depth 4 and 2), down on the 192-row
+on 192- and 384-row tiles (prefetch depth 3 and 2), down on the 192-row
 pieces of 384-row tiles (depth 3).
 
 Routing is set explicitly so that tiles have full, partial and empty pieces
@@ -28,8 +28,9 @@ CASES = {
     "bm384_even": (384, 256, 384, [385, 128, 256, 17], True),             # 4 and 6 steps: no tail
     "bm384_down_tail1": (384, 128, 448, [900, 30, 383], False),          # 2 and 7 steps
     "bm384_short_k": (384, 64, 128, [300, 5, 0, 129], False),            # 1 and 2 steps: fewer than the depth
-    "bm192_tail3": (192, 448, 192, [192, 193, 50, 0, 400], True),        # gate+up 7 steps at depth 4
-    "bm192_tail1": (192, 320, 256, [10, 191, 384, 77], False),           # gate+up 5 steps
+    "bm192_tail3": (192, 448, 192, [192, 193, 50, 0, 400], True),        # gate+up 7 steps at depth 3: tail 1
+    "bm192_tail1": (192, 320, 256, [10, 191, 384, 77], False),           # gate+up 5 steps: tail 2
+    "bm192_short_k": (192, 128, 128, [200, 3, 0, 190], False),           # gate+up 2 steps: fewer than the depth
 }
 
 
