@@ -2,7 +2,7 @@
 output channel, bf16 activations) against the oracle's dequantised weights.
 
 Small cases span several row and column tiles, ragged tails, every tile
-height family (split-K short tiles, 96, the 112-column 160 tile, 192),
+height family (split-K short tiles, 96, the 112-column 160 tile, 192, 384),
 capacity mode and skewed routing; full-size cases check every token, and h
 and y_perm on every row of the busiest expert.
 Tolerance: max|gpu - oracle| / max|oracle| <= 2e-2 (bf16 activations; the
@@ -27,6 +27,11 @@ CASES = {
     "fp8_bm96": ("mixtral_t512_fp8", dict(T=256, d=128, F=192), 96),
     "fp8_bm160": ("mixtral_t512_fp8", dict(T=512, d=256, F=128), 160),
     "fp8_bm192": ("mixtral_t512_fp8", dict(T=512, d=128, E=4, F=192), 192),
+    # ping-pong main loops: gate+up on 192-row tiles with a K loop longer than
+    # its prefetch depth, and both GEMMs on 384-row tiles (K loops of 3 and 5
+    # steps: tails of 1 and 2 past whole rounds)
+    "fp8_bm192_long_k": ("mixtral_t512_fp8", dict(T=700, d=320, E=3, F=192), 192),
+    "fp8_bm384": ("mixtral_t512_fp8", dict(T=900, d=192, E=2, F=320), 384),
     "fp8_capacity": ("capacity_gini0.30", dict(T=300, d=128, E=16, k=4, F=192, capacity=40, weights="e4m3"), 0),
     "fp8_e64_zipf2": ("e64_zipf_a2.0", dict(T=160, d=128, F=192, weights="e4m3"), 0),
 }
