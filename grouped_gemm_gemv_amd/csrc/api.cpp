@@ -106,6 +106,20 @@ bool split_down(const moe_shape_t& s, int BM) {
   return BM == 160 && s.dtype == MOE_BF16 && mean_rows(s) >= kSplitMinRows && (int64_t)s.F * 2 >= 256;
 }
 
+// moe_forward folds the combine into the down GEMM for a batch of at most
+// two (token, slot) entries on the 16-row tile map, one pass: each down
+// workgroup computes its column slice of y for every tile and then the output
+// columns of every token (down_combine_kernel), which saves the combine's
+// launch.  Each workgroup then streams every active expert's weights for its
+// columns, so there are as many workgroups as column tiles instead of tiles
+// times column tiles.  Measured at the Mixtral shape: T = 1 (two tiles) 125.0
+// vs 126.2 us per layer; T = 8 (up to eight tiles) 386.1 vs 383.5, hence the
+// limit.  With 8 wavefronts splitting K instead of 4 the gain at T = 1 was
+// gone (126.3 us).
+bool fused_down_combine(const moe_shape_t& s, int BM) {
+  return BM == 16 && s.capacity == 0 && (int64_t)s.T * s.k <= 2;
+}
+
 int64_t spill_bound(const moe_shape_t& s) { return std::max<int64_t>(0, (int64_t)s.T * s.k - s.capacity); }
 
 // Upper bound on the tiles of one pass: a pass of R_p rows over at most E_p
@@ -389,9 +403,17 @@ moe_status_t enqueue_gate_up(const moe_shape_t& s, const void* x_perm, const voi
 // partial planes are added into y by k_split_finish unless `finish` is false
 // (moe_forward then forms y inside its combine).
 moe_status_t enqueue_down(const moe_shape_t& s, const void* h, const void* wd, const moe_dispatch_t& d, int pass,
-                          void* y, hipStream_t st, const float* sd = nullptr, bool finish = true) {
+                          void* y, hipStream_t st, const float* sd = nullptr, bool finish = true,
+                          void* comb_out = nullptr, const float* comb_w = nullptr) {
   moe::GemmArgs a = gemm_args(s, d, pass, false);
   a.s0 = sd;
+  if (comb_out != nullptr) {
+    a.comb_out = comb_out;
+    a.comb_w = comb_w;
+    a.comb_row_of = d.row_of;
+    a.comb_T = s.T;
+    a.comb_k = s.k;
+  }
   const bool split = split_down(s, d.tile_rows);
   if (split) {
     a.kpart = d.kpart;
@@ -458,6 +480,8 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_rou
   if ((st = enqueue_gate_up(*s, nullptr, w_gate, w_up, v.disp, ps, v.h, stream, x, s_gate, s_up)) != MOE_OK)
     return st;
   const bool split = split_down(*s, v.disp.tile_rows);
+  if (fused_down_combine(*s, v.disp.tile_rows))  // a decode batch: the combine inside the down GEMM
+    return enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream, s_down, true, out, v.topk_w);
   if ((st = enqueue_down(*s, v.h, w_down, v.disp, ps, v.y_perm, stream, s_down, !split)) != MOE_OK) return st;
   if (split)  // y formed from the two K ranges inside the combine
     return hip_status(moe::launch_combine_split(s->dtype, v.disp.kpart, (size_t)p.R * s->d, v.topk_w,

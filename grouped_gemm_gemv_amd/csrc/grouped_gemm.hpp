@@ -1044,6 +1044,78 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Down GEMM of a decode batch with the combine folded in (16-row tile map,
+// one pass).  Workgroup b owns output columns [b BN, b BN + BN) of every
+// tile: it runs the down GEMM's main loop for each tile of the map in turn
+// (the same Gemm, so y is bitwise that of grouped_gemm_kernel), stores y,
+// and once every tile is done weights the rows of each token into its output
+// for those columns exactly as the separate combine does (fp32 fmaf in slot
+// order from 0, one rounding).  It saves the combine's launch; each
+// workgroup streams the weights of every active expert for its columns.
+template <class Tr, class Cfg, bool WQ>
+__global__ __launch_bounds__(64 * Cfg::WN * Cfg::WK) void down_combine_kernel(GemmArgs p) {
+  using G = Gemm<Tr, Cfg::BM, Cfg::WTN, Cfg::WN, Cfg::WK, false, Cfg::PF, Cfg::NTMS, WQ, Cfg::WS>;
+  using Elt = typename Tr::T;
+  constexpr int EPC = Tr::EPC;
+  static_assert(Cfg::RS == 1 && Cfg::PP == 0 && G::BN % EPC == 0, "decode down + combine shape");
+  __shared__ __attribute__((aligned(16))) char st0[G::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[G::STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[G::STAGE];
+  __shared__ __attribute__((aligned(16))) char st3[G::NA > 3 ? G::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st4[G::NA > 4 ? G::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st5[G::NA > 5 ? G::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st6[G::NA > 6 ? G::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char st7[G::NA > 7 ? G::STAGE : 16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nbase = (int)blockIdx.x * G::BN;
+  if (nbase >= p.N) return;
+  char* const all[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
+  const int ntiles = p.n_tiles[0];
+  const int4* map = reinterpret_cast<const int4*>(p.tile_map);
+  for (int i = 0; i < ntiles; ++i) {
+    const int4 ent = map[i];
+    const int mt = p.tile_off[ent.x + 1] - p.tile_off[ent.x];
+    typename G::Ctx c;
+    setup_ctx<G>(c, p, all, ent.x, ent.y, ent.z, nbase, wave, lane);
+    G::template run_ms<G::MSUB>((ent.z + 15) >> 4, mt == 1 && ent.z <= Cfg::BM, c);
+    // the next tile reuses the LDS stages; the last one's y rows are read below
+    __syncthreads();
+  }
+  // combine of this workgroup's columns
+  const size_t row_bytes = (size_t)p.N * sizeof(Elt);
+  const int nch = min(G::BN, p.N - nbase) / EPC;  // 16-byte chunks of the slice
+  const char* y = reinterpret_cast<const char*>(p.out);
+  char* out = reinterpret_cast<char*>(p.comb_out);
+  for (int idx = threadIdx.x; idx < p.comb_T * nch; idx += blockDim.x) {
+    const int t = idx / nch;
+    const size_t off = (size_t)(nbase + (idx - t * nch) * EPC) * sizeof(Elt);
+    float acc[EPC];
+#pragma unroll
+    for (int q = 0; q < EPC; ++q) acc[q] = 0.f;
+    for (int j = 0; j < p.comb_k; ++j) {
+      const int row = p.comb_row_of[(size_t)t * p.comb_k + j];
+      if (row < 0) continue;
+      const float wj = p.comb_w[(size_t)t * p.comb_k + j];
+      float v[EPC];
+      widen<Tr>(*reinterpret_cast<const uint4*>(y + (size_t)row * row_bytes + off), v);
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+    }
+    *reinterpret_cast<uint4*>(out + (size_t)t * row_bytes + off) = narrow<Tr>(acc);
+  }
+}
+
+template <class Tr, bool WQ>
+hipError_t launch_down_combine(const GemmArgs& a, hipStream_t stream) {
+  using Cfg = typename TileCfg<16, false, WQ>::type;
+  constexpr int BN = Cfg::WN * Cfg::WTN;
+  const int grid = (a.N + BN - 1) / BN;
+  hipLaunchKernelGGL((down_combine_kernel<Tr, Cfg, WQ>), dim3((unsigned)grid), dim3(64 * Cfg::WN * Cfg::WK), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 template <class Tr, bool GATED, bool WQ = false>
 hipError_t dispatch_bm(int BM, const GemmArgs& a, hipStream_t stream) {
   if constexpr (GATED && !WQ && std::is_same<Tr, TBF16>::value) {
@@ -1051,6 +1123,9 @@ hipError_t dispatch_bm(int BM, const GemmArgs& a, hipStream_t stream) {
   }
   if constexpr (!GATED && std::is_same<Tr, TBF16>::value) {
     if (BM == 160 && a.kpart != nullptr) return launch_cfg<Tr, Split160, false, WQ, 2>(a, stream);
+  }
+  if constexpr (!GATED) {
+    if (a.comb_out != nullptr) return BM == 16 ? launch_down_combine<Tr, WQ>(a, stream) : hipErrorInvalidValue;
   }
   switch (BM) {
 #define MOE_BM_CASE(bm) \

@@ -106,6 +106,14 @@ struct GemmArgs {
   float* kpart;              // non-null: bf16 down on the 160-row map splits K in two; fp32 partial sums,
                              // plane ks of [2][R][N] (kplane floats per plane)
   size_t kplane;
+  // Down GEMM of a decode batch (16-row tiles, one pass) with the combine
+  // folded in: non-null comb_out makes each workgroup compute its column
+  // slice of y for every tile of the map, store it, and then weight it into
+  // out[t] = sum_j comb_w[t k + j] y[comb_row_of[t k + j]] for that slice.
+  void* comb_out;
+  const float* comb_w;
+  const int32_t* comb_row_of;
+  int comb_T, comb_k;
 };
 
 // y[r] = rounded(part[0][r] + part[1][r]) for every row r with token_of[r] >= 0:
