@@ -27,6 +27,7 @@ CASES = {
     "fp8_bm96": ("mixtral_t512_fp8", dict(T=256, d=128, F=192), 96),
     "fp8_bm160": ("mixtral_t512_fp8", dict(T=512, d=256, F=128), 160),
     "fp8_bm192": ("mixtral_t512_fp8", dict(T=512, d=128, E=4, F=192), 192),
+    "fp8_t1": ("mixtral_t512_fp8", dict(T=1, d=256, F=320), 0),  # the combine inside the down GEMM
     # ping-pong main loops: gate+up on 192-row tiles with a K loop longer than
     # its prefetch depth, and both GEMMs on 384-row tiles (K loops of 3 and 5
     # steps: tails of 1 and 2 past whole rounds)
@@ -95,7 +96,7 @@ def test_fp8_layer_output(runs, case):
     assert ey <= TOL["bf16"] and eo <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("case", ["fp8_ragged", "fp8_capacity", "fp8_bm16"])
+@pytest.mark.parametrize("case", ["fp8_ragged", "fp8_capacity", "fp8_bm16", "fp8_t1"])
 def test_fp8_forward_equals_steps_and_repeats(runs, case):
     import grouped_gemm_gemv_amd as M
     r = runs(case)

@@ -64,6 +64,11 @@ CASES = {
     "f32_t16_e32": ("tiny_f32", dict(T=16, E=32, k=4)),
     "bf16_t12_cap_bias": ("capacity_gini0.30", dict(T=12, d=128, E=16, k=4, F=128, capacity=2)),
     "bf16_t17": ("mixtral_t512", dict(T=17, d=128, F=64)),
+    # one or two (token, slot) entries: moe_forward computes the combine inside
+    # the down GEMM, which the step-by-step path checks bitwise
+    "f32_t1": ("tiny_f32", dict(T=1)),
+    "bf16_t2_k1": ("mixtral_t512", dict(T=2, d=192, k=1, F=320)),
+    "bf16_t1_k1": ("mixtral_t512", dict(T=1, d=128, E=4, k=1, F=64)),
     # 384-row tiles, worked in pieces (three of 128 rows by gate+up, two of
     # 192 by down): experts of two and three map tiles with ragged and empty
     # last pieces, the capacity split, and fp32
