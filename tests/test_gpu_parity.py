@@ -307,6 +307,26 @@ def test_route_every_expert_range(E, k, dt):
     assert differ <= 1
 
 
+@pytest.mark.parametrize("E,k,dt", [(8, 2, "bf16"), (24, 3, "f32"), (64, 6, "bf16"), (100, 6, "bf16")])
+def test_route_large_batch(E, k, dt):
+    """Batches of 2048 tokens and more: 16 tokens per router workgroup at each
+    router tile; T = 2100 leaves a last workgroup of 4 tokens."""
+    _need_gpu()
+    import grouped_gemm_gemv_amd as M
+    base = "tiny_f32" if dt == "f32" else "mixtral_t512"
+    wl = get_workload(base, T=2100, d=128, E=E, k=k, F=64, wr_std=0.5 if dt == "bf16" else 1.0)
+    inp = make_inputs(wl, 4, experts=False)
+    shape = _shape(wl)
+    ids = torch.empty((wl.T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((wl.T, k), dtype=torch.float32, device="cuda")
+    print(f"\n[gpu parity] route T={wl.T} E={E} k={k} {dt}", flush=True)
+    M.moe_route(shape, dev(inp.x), dev(inp.wr), None, ids, w)
+    torch.cuda.synchronize()
+    logits = O.router_logits(inp.x, inp.wr, wl.dtype)
+    differ = check_routing(ids.cpu().numpy(), w.cpu().numpy().astype(np.float64), logits, k)
+    assert differ <= wl.T // 100  # tokens whose k-th and (k+1)-th logits nearly tie
+
+
 @pytest.mark.parametrize("C", [0, 200])
 def test_dispatch_multiblock_path(C):
     """T*k above the single-workgroup limit: count + scan + scatter kernels."""
